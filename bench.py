@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA paged-latent decode hot path on one MI355X.
+
+One step = one full decode call over one batch of synthetic input (the
+split-KV partial kernel and, with more than one split, the LSE merge
+kernel), inputs already resident in HBM.  Default workload: the 80k-token
+MTP-3 fp8 decode (B=64, H=32, q_len=4, block 64), the configuration the
+target is quoted on.  Prints ONE JSON line on stdout; details go to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0                  # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}   # dense MFMA
+FLOPS_PER_PAIR = 2 * 576 + 2 * 512     # QK over 576 features + PV over 512
+DEFAULT_WORKLOAD = "mtp3_b64_h32_kv80k_fp8"
+KERNEL_SOURCES = [os.path.join(ROOT, "mla_paged_latent_03_amd", "csrc", f)
+                  for f in ("mla_decode_kernels.hip", "mla_decode_api.cpp", "mla_decode_internal.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_cost(inp):
+    """Bytes the method must move and FLOPs it must do, from the host copy of
+    the lengths / indices (tokens attended read once per sequence)."""
+    lens = inp.seq_lens.cpu().numpy().astype(np.int64)
+    B, T, H = inp.B, inp.T, inp.H
+    elt = 1 if inp.kv_dtype == "fp8" else 2
+    out_elt = 4 if inp.out_dtype == "f32" else 2
+    rows = B * T * H
+    if inp.topk_indices is None:
+        kv_tokens = int(lens.sum())
+        pairs = sum(H * max(0, int(L) - T + t + 1) for L in lens for t in range(T))
+        meta = int(((lens + 63) // 64).sum()) * 4                       # block-table entries
+    else:
+        idx = inp.topk_indices.cpu().numpy()
+        valid = (idx >= 0) & (idx < lens[:, None, None])
+        kv_tokens = int(valid.sum())                                   # gathered rows (per query token)
+        pairs = H * kv_tokens
+        meta = idx.size * 4 * 2                                        # indices + their block-table entries
+    kv_bytes = kv_tokens * 576 * elt
+    q_bytes = rows * 576 * elt
+    out_bytes = rows * 512 * out_elt + rows * 4
+    flops = pairs * FLOPS_PER_PAIR
+    return dict(kv_bytes=kv_bytes, q_bytes=q_bytes, out_bytes=out_bytes, meta_bytes=meta,
+                total_bytes=kv_bytes + q_bytes + out_bytes + meta, partial_bytes=kv_bytes + q_bytes + meta,
+                flops=flops, kv_tokens=kv_tokens)
+
+
+def cpu_baseline(inp, seconds: float):
+    """The fp64 oracle, as it stands, on a bounded sample of rows; scaled to
+    the whole call (every row costs the same visible-list work for the
+    uniform-length workloads, and the sample is drawn uniformly otherwise)."""
+    import oracle
+    from mla_paged_latent_03_amd import workloads as wl
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cpu = inp.to("cpu")
+    args = dict(q_nope=wl.as_numpy_bits(cpu.q_nope), q_pe=wl.as_numpy_bits(cpu.q_pe),
+                kv_cache=wl.as_numpy_bits(cpu.kv_cache), block_table=cpu.block_table.numpy(),
+                seq_lens=cpu.seq_lens.numpy())
+    topk = None if cpu.topk_indices is None else cpu.topk_indices.numpy()
+    total = inp.B * inp.T * inp.H
+    rng = np.random.default_rng(0)
+    n = min(total, max(cores, 16))
+    t_first = None
+    while True:
+        rows = np.sort(rng.choice(total, size=n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.decode(args["q_nope"], args["q_pe"], args["kv_cache"], args["block_table"], args["seq_lens"],
+                      softmax_scale=inp.softmax_scale, q_scale=inp.q_scale, kv_scale=inp.kv_scale,
+                      topk_indices=topk, rows=rows, threads=cores)
+        dt = time.perf_counter() - t0
+        if t_first is None and dt < seconds / 4 and n < total:
+            t_first = dt
+            n = int(min(total, max(n + 1, n * seconds / max(dt, 1e-3))))
+            continue
+        break
+    us_per_call = dt * (total / n) * 1e6
+    return dict(value=us_per_call, unit="us/call", cores=cores, kind="oracle",
+                sample="%d of %d output rows (random, seed 0), fp64 oracle, %.1f s wall, scaled to all rows"
+                       % (n, total, dt))
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch of the partial kernel from the rocprofv3 PMC runs
+    recorded for this workload, if they were taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build's hot path has no multi-GPU form "
+              "(the sequence-sharded design is described, not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_paged_latent_03_amd import binding, workloads as wl
+
+    binding.load()
+    dev = torch.device("cuda:0")
+    log("[bench] drawing %s on %s" % (args.workload, dev))
+    inp = wl.workload(args.workload, device=dev)
+    fp8 = inp.kv_dtype == "fp8"
+    S = args.splits or binding.num_kv_splits(inp.B, inp.T, inp.H, inp.max_seq_len, inp.K, fp8)
+    out = torch.empty((inp.B, inp.T, inp.H, 512), device=dev,
+                      dtype=torch.float32 if inp.out_dtype == "f32" else torch.bfloat16)
+    lse = torch.empty((inp.B, inp.T, inp.H), device=dev, dtype=torch.float32)
+    ws_bytes = binding.workspace_size(inp.B, inp.T, inp.H, inp.max_seq_len, inp.K, fp8, S)
+    ws = torch.empty(max(1, (ws_bytes + 3) // 4), device=dev, dtype=torch.float32) if ws_bytes else None
+    stream = torch.cuda.current_stream()
+
+    def step(stage1_only=False):
+        o = None if stage1_only else out
+        l = None if stage1_only else lse
+        if inp.K > 0:
+            binding.mla_sparse_decode(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens,
+                                      inp.topk_indices, inp.max_seq_len, inp.softmax_scale, o, l, ws, S, stream)
+        elif fp8:
+            binding.mla_decode_fp8(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens,
+                                   inp.max_seq_len, inp.softmax_scale, inp.q_scale, inp.kv_scale, o, l, ws, S,
+                                   stream)
+        else:
+            binding.mla_decode(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens,
+                               inp.max_seq_len, inp.softmax_scale, o, l, ws, S, stream)
+
+    def timed(n, stage1_only=False):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            step(stage1_only)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n           # ms per call
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("[bench] timing %d steps (splits=%d)" % (args.steps, S))
+    ms_step = timed(args.steps)
+    # The dominant (partial) kernel alone: with one split it is the whole call.
+    ms_partial = timed(args.steps, stage1_only=True) if S > 1 else ms_step
+    if not bool(torch.isfinite(out.float()).all()):
+        raise RuntimeError("non-finite output")
+
+    cost = algorithmic_cost(inp)
+    kdt = "fp8" if fp8 else "bf16"
+    t_hbm = cost["total_bytes"] / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = cost["flops"] / (MFMA_PEAK_TFLOPS[kdt] * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    part_bytes = cost["partial_bytes"] + (cost["out_bytes"] if S == 1 else 0)
+    if bound == "hbm":
+        achieved = part_bytes / (ms_partial * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4))
+    else:
+        achieved = cost["flops"] / (ms_partial * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_PEAK_TFLOPS[kdt], unit="TFLOP/s",
+                    frac=round(achieved / MFMA_PEAK_TFLOPS[kdt], 4))
+    roof["kernel"] = "mla_partial_kernel"
+    roof["us_per_launch"] = round(ms_partial * 1e3, 2)
+    roof["traffic"] = load_traffic(args.workload)
+
+    step_s = ms_step * 1e-3
+    res = {
+        "metric": "MLA decode us/call + achieved HBM TB/s & MFMA TFLOP/s as % of roofline",
+        "value": round(ms_step * 1e3, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "data": "synthetic (seeded N(0,1) values, shuffled pages)",
+        "config": {"workload": args.workload, "batch": inp.B, "heads": inp.H, "q_len": inp.T,
+                   "max_seq_len": inp.max_seq_len, "block_size": 64, "topk": inp.K, "kv_splits": S,
+                   "out_dtype": inp.out_dtype},
+        "step": {"hbm_TBps": round(cost["total_bytes"] / step_s / 1e12, 3),
+                 "mfma_TFLOPs": round(cost["flops"] / step_s / 1e12, 1),
+                 "frac_hbm": round(cost["total_bytes"] / step_s / 1e12 / (HBM_PEAK_GBPS / 1e3), 4),
+                 "frac_mfma": round(cost["flops"] / step_s / 1e12 / MFMA_PEAK_TFLOPS[kdt], 4),
+                 "roofline_frac": round(max(t_hbm, t_mfma) / step_s, 4),
+                 "algorithmic_bytes": cost["total_bytes"], "algorithmic_flops": cost["flops"]},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on a row sample, ~%.0f s)" % args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

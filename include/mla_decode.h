@@ -1,0 +1,205 @@
+/*
+ * mla_decode.h - C ABI of the MI355X (gfx950) MLA decode library
+ * (libmla_decode.so).
+ *
+ * Operation.  Multi-head latent attention decode in absorbed form over a
+ * paged latent KV cache.  Every cached token is ONE 576-wide vector shared by
+ * all heads: a 512-wide latent c (kv_lora_rank) followed by a 64-wide rope
+ * part r.  The pages size the split-KV partial as kv_lora_rank + 1 floats
+ * (vLLM PR #46819 digest, "Key code excerpt") and fix the DeepSeek-R1 head
+ * dims at 128 no-rope + 64 rope, so the default softmax scale is 1/sqrt(192)
+ * (vLLM PR #41778 digest, "Risks and impact" item 4).  For query row
+ * (b, t, h) and each visible token j:
+ *
+ *     s_j = softmax_scale * ( <q_nope[b,t,h,:], c_j> + <q_pe[b,t,h,:], r_j> )
+ *     out[b,t,h,:] = sum_j softmax(s)_j * c_j          (latent space, 512 wide)
+ *     lse[b,t,h]   = ln sum_j exp(s_j)                  (natural log)
+ *
+ * Visible tokens.  Dense calls: q_len = T draft tokens per sequence
+ * (multi-token prediction, vLLM PR #41778 digest, "Motivation"); seq_lens[b]
+ * counts the cache INCLUDING the T draft tokens, and draft token t sees
+ * positions 0 .. seq_lens[b] - T + t (causal inside the draft).  Sparse
+ * calls: token t of sequence b sees the positions listed in
+ * topk_indices[b, t, 0..K) (index_topk per query token, vLLM PR #47327
+ * digest, "Key code excerpt"); entries outside [0, seq_lens[b]) - the -1
+ * padding included - are skipped, duplicates count as listed, and no
+ * causal mask is added.  A row with no visible token gets out = 0 and
+ * lse = -inf.
+ *
+ * Paging.  Position j of sequence b lives in page block_table[b, j / 64],
+ * slot j % 64, of kv_cache [num_blocks, 64, 576] (row-major, 576 contiguous).
+ * Only block_size = 64 is supported.
+ *
+ * Split-KV.  A call may cut each sequence's tokens into num_kv_splits
+ * page-aligned chunks, write one fp32 partial per (b, row, split) into the
+ * caller's workspace [B, T*H, splits, 513] (512 normalized outputs, then the
+ * chunk's lse) and merge them by log-sum-exp in a second kernel, as in the
+ * two-stage Triton MLA decode (vLLM PR #46819 digest, "Implementation"
+ * items 1-3).  With one split the first kernel writes out and lse itself
+ * and the workspace is not touched.
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
+ *    row-major, on the current HIP device.  The library allocates nothing,
+ *    keeps no per-call state and caches only the device's compute-unit
+ *    count.
+ *  - Calls enqueue on `stream` (a hipStream_t; NULL = the null stream) and
+ *    return without synchronizing; they are safe to capture in a HIP graph.
+ *  - Scales are read on every call and never cached (the pages record a
+ *    bug where cached scales kept profiling-time values: vLLM PR #41778
+ *    digest, "Review highlights").
+ *  - q_len is uniform across the batch; non-uniform batches are not
+ *    representable (the same review flags an unsafe fallback for them).
+ *  - Errors the host can see are returned BEFORE any launch, and nothing is
+ *    enqueued: bad dims, T outside [1, 8], block_size != 64, a NULL required
+ *    pointer, num_kv_splits outside [0, MLA_MAX_KV_SPLITS], a workspace
+ *    smaller than mla_workspace_size().  A failed launch returns MLA_ERR_HIP.
+ *  - Device data is not validated on the host.  In the kernels, seq_lens are
+ *    clamped to [0, max_blocks_per_seq * 64], page numbers outside
+ *    [0, num_blocks) read as zero vectors, and block-table slots past a
+ *    sequence's last page are never read.  seq_lens[b] must not exceed
+ *    max_seq_len (the host bound that sizes the splits); tokens beyond
+ *    num_kv_splits chunks of the bound are not attended.
+ *  - out and lse may not alias any input or the workspace.
+ *
+ * Two-stage use.  A decode call with out = NULL and lse = NULL stops after
+ * the first stage: it writes the split partials into the workspace and
+ * launches nothing else (this needs an explicit num_kv_splits >= 2).
+ * mla_merge_partials() then runs the second stage on such a workspace.  The
+ * stages can thus be timed, overlapped or fed with partials from elsewhere
+ * (for instance chunks of a sequence held on other GPUs), while the one-call
+ * form stays the common path.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1,
+  MLA_ERR_UNSUPPORTED = 2,
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MLA_ERR_HIP = 4
+} mla_status_t;
+
+/* Output element type of `out`. */
+enum { MLA_OUT_BF16 = 0, MLA_OUT_F32 = 1 };
+
+#define MLA_KV_LORA_RANK 512
+#define MLA_ROPE_DIM 64
+#define MLA_TOKEN_DIM 576
+#define MLA_BLOCK_SIZE 64
+#define MLA_MAX_Q_LEN 8
+#define MLA_MAX_KV_SPLITS 256
+
+/* Static text for a status code (never NULL). */
+const char* mla_status_string(mla_status_t status);
+
+/*
+ * Split count the library picks for a call when num_kv_splits = 0.  It fills
+ * the chip's compute units with (sequence, row block, split) work units and
+ * splits further only while the split partials stay a small fraction of the
+ * KV bytes.  Deterministic in its arguments; topk = 0 means a dense call,
+ * otherwise a sparse call with that K.  Returns 0 on invalid arguments.
+ */
+int mla_num_kv_splits(int batch, int q_len, int num_heads, int max_seq_len, int topk,
+                      int kv_fp8);
+
+/*
+ * Workspace bytes a call needs: batch * q_len * num_heads * splits * 513 * 4,
+ * or 0 when the call runs with one split.  num_kv_splits = 0 means the
+ * heuristic choice above.  Returns 0 for invalid arguments as well; pass the
+ * same arguments to the decode call.
+ */
+size_t mla_workspace_size(int batch, int q_len, int num_heads, int max_seq_len, int topk,
+                          int kv_fp8, int num_kv_splits);
+
+/*
+ * The Triton MLA decode's split rule, kept for comparison:
+ * min(next_pow2(max(1, max_seq_len / 512)), 2 * sm_count)  (vLLM PR #46819
+ * digest, "Key code excerpt").  Not used by the decode calls.  Returns 0 on
+ * invalid arguments.
+ */
+int mla_num_kv_splits_baseline(int max_seq_len, int sm_count);
+
+/*
+ * Dense bf16 decode.
+ *   q_nope      [B, T, H, 512] bf16   absorbed no-rope query
+ *   q_pe        [B, T, H, 64]  bf16   rope query
+ *   kv_cache    [num_blocks, 64, 576] bf16
+ *   block_table [B, max_blocks_per_seq] int32
+ *   seq_lens    [B] int32, tokens in the cache per sequence (draft included)
+ *   max_seq_len host upper bound of seq_lens (sizes the splits)
+ *   out         [B, T, H, 512] in out_dtype (MLA_OUT_BF16 or MLA_OUT_F32), or
+ *               NULL together with lse for the first stage only (see above)
+ *   lse         [B, T, H] fp32, or NULL
+ *   workspace   >= mla_workspace_size(B, T, H, max_seq_len, 0, 0, num_kv_splits)
+ *               bytes (may be NULL when that size is 0); contents on entry
+ *               are ignored and left undefined on return
+ *   num_kv_splits 0 = library choice, else 1 .. MLA_MAX_KV_SPLITS
+ */
+mla_status_t mla_decode(const void* q_nope, const void* q_pe, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* seq_lens, int batch,
+                        int q_len, int num_heads, int num_blocks, int block_size,
+                        int max_blocks_per_seq, int max_seq_len, float softmax_scale,
+                        void* out, int out_dtype, float* lse, void* workspace,
+                        size_t workspace_bytes, int num_kv_splits, void* stream);
+
+/*
+ * Dense fp8 decode.  q_nope, q_pe and kv_cache hold OCP e4m3fn bytes with
+ * one per-tensor dequant scale each: the query value is byte * q_scale (one
+ * scale for q_nope and q_pe together) and the cache value byte * kv_scale
+ * (fp8 decode with dequant scales, vLLM PR #41778 digest, "Implementation"
+ * item 1).  Logits use softmax_scale * q_scale * kv_scale; the output is the
+ * dequantized latent average, i.e. it carries kv_scale.  Inside, both
+ * products run on fp8 MFMA; the softmax probabilities are scaled by 2^8
+ * before their e4m3 rounding so they stay in the format's normal range.
+ * Other arguments as mla_decode; workspace sized with kv_fp8 = 1.
+ */
+mla_status_t mla_decode_fp8(const void* q_nope, const void* q_pe, const void* kv_cache,
+                            const int32_t* block_table, const int32_t* seq_lens, int batch,
+                            int q_len, int num_heads, int num_blocks, int block_size,
+                            int max_blocks_per_seq, int max_seq_len, float softmax_scale,
+                            float q_scale, float kv_scale, void* out, int out_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, int num_kv_splits,
+                            void* stream);
+
+/*
+ * Top-k sparse bf16 decode.  topk_indices [B, T, K] int32 lists, per query
+ * token, the cache positions it attends (shared by all heads); see
+ * "Visible tokens" above.  K >= 1.  Workspace sized with topk = K.  Other
+ * arguments as mla_decode.
+ */
+mla_status_t mla_sparse_decode(const void* q_nope, const void* q_pe, const void* kv_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* topk_indices, int topk, int batch, int q_len,
+                               int num_heads, int num_blocks, int block_size,
+                               int max_blocks_per_seq, int max_seq_len, float softmax_scale,
+                               void* out, int out_dtype, float* lse, void* workspace,
+                               size_t workspace_bytes, int num_kv_splits, void* stream);
+
+/*
+ * Second stage alone: log-sum-exp merge of split partials.
+ *   workspace  [rows, num_kv_splits, 513] fp32, as a decode call writes it
+ *              (rows = B * T * H; per (row, split): 512 normalized outputs
+ *              then the split's lse, -inf for a split that saw no token)
+ *   out        [rows, 512] in out_dtype; lse [rows] fp32 or NULL
+ * out = sum_s exp(lse_s - lse) * O_s with lse = ln sum_s exp(lse_s), the
+ * merge of the two-stage Triton MLA decode (vLLM PR #46819 digest,
+ * "Implementation" items 1-3); rows whose splits are all empty get 0 and
+ * -inf.  num_kv_splits in [1, MLA_MAX_KV_SPLITS].
+ */
+mla_status_t mla_merge_partials(const float* workspace, int64_t rows, int num_kv_splits, void* out,
+                                int out_dtype, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

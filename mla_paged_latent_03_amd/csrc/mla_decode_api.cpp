@@ -1,0 +1,269 @@
+// C ABI of libmla_decode.so: argument checks, the split planner, workspace
+// sizing and the two launches.  Declarations and contracts: mla_decode.h.
+#include "../../include/mla_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "mla_decode_internal.h"
+
+namespace {
+
+using mla::kNumCUs;
+using mla::kPartialWidth;
+using mla::kSparseChunkMax;
+
+struct Plan {
+  int R = 0;        // query rows per sequence, T * H
+  int rg = 1;       // waves per workgroup (32 rows each)
+  int n_rb = 1;     // row blocks per (sequence, split)
+  int n_hb = 1;     // sparse: head blocks per draft token
+  int S = 1;        // KV splits
+  int chunk = 1;    // dense: pages per split; sparse: indices per split
+  size_t ws_bytes = 0;
+};
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+int rg_for_rows(int rows) { return rows <= 32 ? 1 : (rows <= 64 ? 2 : 4); }
+
+// Resident workgroups per CU for a row-group width (LDS ring: 4 x 36 KiB for
+// 4 waves, 2 x 36 KiB otherwise).
+int wg_per_cu(int rg) { return rg == 4 ? 1 : 2; }
+
+bool dims_ok(int B, int T, int H, int max_seq_len, int topk) {
+  return B >= 0 && B <= (1 << 20) && T >= 1 && T <= MLA_MAX_Q_LEN && H >= 1 && H <= 1024 &&
+         max_seq_len >= 0 && max_seq_len <= (1 << 26) && topk >= 0 && topk <= (1 << 24);
+}
+
+// Split planning.  Work unit = (sequence, row block, split).  Fill the chip's
+// resident workgroup slots once; split KV only while the fp32 partials
+// (written and read back) stay under 1/16 of the KV bytes they summarize;
+// when that limit leaves slots idle, cut the rows into narrower blocks
+// instead (their KV re-reads are served from the shared L2 of one XCD).
+bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req_splits, Plan* pl) {
+  if (!dims_ok(B, T, H, max_seq_len, topk) || req_splits < 0 || req_splits > MLA_MAX_KV_SPLITS) return false;
+  Plan p;
+  p.R = T * H;
+  const bool sparse = topk > 0;
+  const int rows_blk = sparse ? H : p.R;                    // rows sharing one token list
+  const double kv_token_bytes = MLA_TOKEN_DIM * (fp8 ? 1.0 : 2.0);
+  // Tokens of a split one sequence reads, and the most splits that pays for itself.
+  const int64_t tokens = sparse ? (int64_t)topk : (int64_t)max_seq_len;
+  const double part_bytes = (double)rows_blk * kPartialWidth * 4.0 * 2.0;  // write + read
+  const int64_t min_tokens_per_split = (int64_t)std::ceil(16.0 * part_bytes / kv_token_bytes);
+  int s_ovh = (int)(tokens / (min_tokens_per_split > 0 ? min_tokens_per_split : 1));
+  if (s_ovh < 1) s_ovh = 1;
+  const int s_min = sparse ? ceil_div(topk, kSparseChunkMax) : 1;   // LDS index table capacity
+
+  int rg = rg_for_rows(rows_blk);
+  int S = 1;
+  for (;;) {
+    const int rb_rows = 32 * rg;
+    const int n_blk = ceil_div(rows_blk, rb_rows);
+    const int64_t units = (int64_t)B * (sparse ? T : 1) * n_blk;
+    const int64_t slots = (int64_t)kNumCUs * wg_per_cu(rg);
+    const int s_fill = units > 0 ? ceil_div(slots, units) : 1;
+    S = s_fill < s_ovh ? s_fill : s_ovh;
+    if (s_fill <= s_ovh || rg == 1) break;
+    rg >>= 1;
+  }
+  if (S < 1) S = 1;
+  if (S > MLA_MAX_KV_SPLITS) S = MLA_MAX_KV_SPLITS;
+  if (req_splits > 0) S = req_splits;
+  if (S < s_min) {
+    if (req_splits > 0) return false;   // K / splits would exceed the index table
+    S = s_min;
+  }
+  p.rg = rg;
+  const int rb_rows = 32 * rg;
+  if (sparse) {
+    p.n_hb = ceil_div(H, rb_rows);
+    p.n_rb = T * p.n_hb;
+    int c = ceil_div(topk, S);
+    c = ceil_div(c, 64) * 64;
+    if (c > kSparseChunkMax) return false;
+    p.chunk = c;
+  } else {
+    p.n_rb = ceil_div(p.R, rb_rows);
+    const int max_pages = ceil_div(max_seq_len, MLA_BLOCK_SIZE);
+    p.chunk = max_pages > 0 ? ceil_div(max_pages, S) : 1;
+  }
+  p.S = S;
+  p.ws_bytes = S > 1 ? (size_t)B * p.R * S * kPartialWidth * sizeof(float) : 0;
+  *pl = p;
+  return true;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+enum class Kind { kBf16, kFp8, kSparse };
+
+mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv_cache,
+                 const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk_indices,
+                 int topk, int B, int T, int H, int NB, int block_size, int MB, int max_seq_len,
+                 float softmax_scale, float q_scale, float kv_scale, void* out, int out_dtype, float* lse,
+                 void* workspace, size_t workspace_bytes, int num_kv_splits, void* stream) {
+  const bool fp8 = kind == Kind::kFp8;
+  const bool sparse = kind == Kind::kSparse;
+  if (block_size != MLA_BLOCK_SIZE) return MLA_ERR_UNSUPPORTED;
+  if (!dims_ok(B, T, H, max_seq_len, sparse ? topk : 0)) return MLA_ERR_INVALID_ARGUMENT;
+  if (sparse && topk < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (NB < 0 || MB < 1 || (int64_t)NB * MLA_BLOCK_SIZE > INT32_MAX) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_kv_splits < 0 || num_kv_splits > MLA_MAX_KV_SPLITS) return MLA_ERR_INVALID_ARGUMENT;
+  if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale) || !std::isfinite(q_scale) || !std::isfinite(kv_scale) || q_scale <= 0.f ||
+      kv_scale <= 0.f)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (B == 0) return MLA_OK;
+  const bool stage1_only = out == nullptr && lse == nullptr;
+  if (out == nullptr && lse != nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (stage1_only && num_kv_splits < 2) return MLA_ERR_INVALID_ARGUMENT;
+  if (!q_nope || !q_pe || !block_table || !seq_lens || (NB > 0 && !kv_cache) || (sparse && !topk_indices))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv_cache) || !aligned16(out))
+    return MLA_ERR_INVALID_ARGUMENT;
+  Plan pl;
+  if (!make_plan(B, T, H, max_seq_len, sparse ? topk : 0, fp8, num_kv_splits, &pl))
+    return sparse ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARGUMENT;
+  if (pl.ws_bytes > 0) {
+    if (workspace_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned16(workspace)) return MLA_ERR_INVALID_ARGUMENT;
+  }
+
+  mla::PartialParams p{};
+  p.q_nope = (const uint8_t*)q_nope;
+  p.q_pe = (const uint8_t*)q_pe;
+  p.kv = (const uint8_t*)kv_cache;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.topk = sparse ? topk_indices : nullptr;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.R = pl.R;
+  p.NB = NB;
+  p.MB = MB;
+  p.K = sparse ? topk : 0;
+  p.n_rb = pl.n_rb;
+  p.n_hb = pl.n_hb;
+  p.chunk = pl.chunk;
+  p.S = pl.S;
+  const int64_t units = (int64_t)B * pl.S * pl.n_rb;
+  if (units > (int64_t)1 << 30) return MLA_ERR_INVALID_ARGUMENT;
+  p.n_units = (int)units;
+  const float log2e = 1.4426950408889634f;
+  p.qk_scale = fp8 ? softmax_scale * log2e * q_scale * kv_scale : softmax_scale * log2e;
+  p.out_scale = fp8 ? kv_scale : 1.0f;
+  p.out = out;
+  p.out_f32 = out_dtype == MLA_OUT_F32;
+  p.lse = lse;
+  p.ws = pl.S > 1 ? (float*)workspace : nullptr;
+  const int grid = (int)((units + 7) / 8 * 8);
+  hipStream_t st = (hipStream_t)stream;
+  const bool resid = fp8 && (int64_t)pl.chunk * MLA_BLOCK_SIZE <= mla::kFp8ResidualMaxUnitTokens;
+  if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, resid, grid, st) != hipSuccess) return MLA_ERR_HIP;
+  if (pl.S > 1 && !stage1_only) {
+    mla::MergeParams m{};
+    m.ws = (const float*)workspace;
+    m.n_rows = (int64_t)B * pl.R;
+    m.S = pl.S;
+    m.out = out;
+    m.out_f32 = p.out_f32;
+    m.lse = lse;
+    if (mla::launch_merge_kernel(m, st) != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+int mla_num_kv_splits(int batch, int q_len, int num_heads, int max_seq_len, int topk, int kv_fp8) {
+  Plan pl;
+  if (!make_plan(batch, q_len, num_heads, max_seq_len, topk, kv_fp8 != 0, 0, &pl)) return 0;
+  return pl.S;
+}
+
+size_t mla_workspace_size(int batch, int q_len, int num_heads, int max_seq_len, int topk, int kv_fp8,
+                          int num_kv_splits) {
+  Plan pl;
+  if (!make_plan(batch, q_len, num_heads, max_seq_len, topk, kv_fp8 != 0, num_kv_splits, &pl)) return 0;
+  return pl.ws_bytes;
+}
+
+int mla_num_kv_splits_baseline(int max_seq_len, int sm_count) {
+  if (max_seq_len < 0 || sm_count < 1) return 0;
+  const int min_work_per_split = 512, occupancy_multiplier = 2;
+  int ideal = max_seq_len / min_work_per_split;
+  if (ideal < 1) ideal = 1;
+  int pow2 = 1;
+  while (pow2 < ideal) pow2 <<= 1;
+  const int cap = sm_count * occupancy_multiplier;
+  return pow2 < cap ? pow2 : cap;
+}
+
+mla_status_t mla_decode(const void* q_nope, const void* q_pe, const void* kv_cache, const int32_t* block_table,
+                        const int32_t* seq_lens, int batch, int q_len, int num_heads, int num_blocks,
+                        int block_size, int max_blocks_per_seq, int max_seq_len, float softmax_scale, void* out,
+                        int out_dtype, float* lse, void* workspace, size_t workspace_bytes, int num_kv_splits,
+                        void* stream) {
+  return run(Kind::kBf16, q_nope, q_pe, kv_cache, block_table, seq_lens, nullptr, 0, batch, q_len, num_heads,
+             num_blocks, block_size, max_blocks_per_seq, max_seq_len, softmax_scale, 1.0f, 1.0f, out, out_dtype,
+             lse, workspace, workspace_bytes, num_kv_splits, stream);
+}
+
+mla_status_t mla_decode_fp8(const void* q_nope, const void* q_pe, const void* kv_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, int batch, int q_len, int num_heads, int num_blocks,
+                            int block_size, int max_blocks_per_seq, int max_seq_len, float softmax_scale,
+                            float q_scale, float kv_scale, void* out, int out_dtype, float* lse, void* workspace,
+                            size_t workspace_bytes, int num_kv_splits, void* stream) {
+  return run(Kind::kFp8, q_nope, q_pe, kv_cache, block_table, seq_lens, nullptr, 0, batch, q_len, num_heads,
+             num_blocks, block_size, max_blocks_per_seq, max_seq_len, softmax_scale, q_scale, kv_scale, out,
+             out_dtype, lse, workspace, workspace_bytes, num_kv_splits, stream);
+}
+
+mla_status_t mla_sparse_decode(const void* q_nope, const void* q_pe, const void* kv_cache,
+                               const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk_indices,
+                               int topk, int batch, int q_len, int num_heads, int num_blocks, int block_size,
+                               int max_blocks_per_seq, int max_seq_len, float softmax_scale, void* out,
+                               int out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                               int num_kv_splits, void* stream) {
+  return run(Kind::kSparse, q_nope, q_pe, kv_cache, block_table, seq_lens, topk_indices, topk, batch, q_len,
+             num_heads, num_blocks, block_size, max_blocks_per_seq, max_seq_len, softmax_scale, 1.0f, 1.0f, out,
+             out_dtype, lse, workspace, workspace_bytes, num_kv_splits, stream);
+}
+
+mla_status_t mla_merge_partials(const float* workspace, int64_t rows, int num_kv_splits, void* out, int out_dtype,
+                                float* lse, void* stream) {
+  if (rows < 0 || rows > ((int64_t)1 << 40) || num_kv_splits < 1 || num_kv_splits > MLA_MAX_KV_SPLITS)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return MLA_OK;
+  if (!workspace || !out || !aligned16(workspace) || !aligned16(out)) return MLA_ERR_INVALID_ARGUMENT;
+  mla::MergeParams m{};
+  m.ws = workspace;
+  m.n_rows = rows;
+  m.S = num_kv_splits;
+  m.out = out;
+  m.out_f32 = out_dtype == MLA_OUT_F32;
+  m.lse = lse;
+  if (mla::launch_merge_kernel(m, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+}  // extern "C"

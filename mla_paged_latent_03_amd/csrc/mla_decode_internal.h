@@ -1,0 +1,53 @@
+// Internal declarations shared by the host launcher and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kLatentDim = 512;
+constexpr int kRopeDim = 64;
+constexpr int kTokenDim = 576;
+constexpr int kPage = 64;
+constexpr int kPartialWidth = kLatentDim + 1;   // normalized outputs, then the chunk's lse
+constexpr int kSparseChunkMax = 2048;           // top-k entries one workgroup handles
+constexpr int kNumCUs = 256;                    // MI355X compute units
+
+struct PartialParams {
+  const uint8_t* q_nope;        // [B, T, H, 512] bf16 or e4m3 bytes
+  const uint8_t* q_pe;          // [B, T, H, 64]
+  const uint8_t* kv;            // [NB, 64, 576]
+  const int32_t* block_table;   // [B, MB]
+  const int32_t* seq_lens;      // [B]
+  const int32_t* topk;          // [B, T, K] (sparse) or null
+  int B, T, H, R, NB, MB, K;
+  int n_rb;                     // row blocks per (sequence, split)
+  int n_hb;                     // sparse: head blocks per draft token
+  int chunk;                    // dense: pages per split; sparse: indices per split
+  int S;                        // splits
+  int n_units;                  // B * S * n_rb
+  float qk_scale;               // softmax_scale * log2(e) [* q_scale * kv_scale]
+  float out_scale;              // kv_scale (fp8) or 1
+  void* out;                    // [B, T, H, 512] bf16 / f32 (one split)
+  int out_f32;
+  float* lse;                   // [B, T, H] or null (one split)
+  float* ws;                    // [B, R, S, 513] (more than one split)
+};
+
+struct MergeParams {
+  const float* ws;              // [n_rows, S, 513]
+  int64_t n_rows;               // B * R
+  int S;
+  void* out;
+  int out_f32;
+  float* lse;
+};
+
+// fp8 work units of at most this many tokens use the residual product.
+constexpr int kFp8ResidualMaxUnitTokens = 8192;
+
+hipError_t launch_partial_kernel(const PartialParams& p, bool fp8, bool sparse, int rg, bool resid, int grid,
+                                 hipStream_t stream);
+hipError_t launch_merge_kernel(const MergeParams& p, hipStream_t stream);
+
+}  // namespace mla

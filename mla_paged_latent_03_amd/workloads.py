@@ -55,6 +55,11 @@ class DecodeInputs:
     name: str = "custom"
     seed: int = 0
     meta: dict = field(default_factory=dict)
+    max_len: Optional[int] = None   # host copy of max(seq_lens); taken once, never during graph capture
+
+    def __post_init__(self):
+        if self.max_len is None:
+            self.max_len = int(self.seq_lens.max().item()) if self.seq_lens.numel() else 0
 
     @property
     def B(self) -> int:
@@ -86,7 +91,7 @@ class DecodeInputs:
 
     @property
     def max_seq_len(self) -> int:
-        return int(self.seq_lens.max().item()) if self.B else 0
+        return self.max_len
 
     def to(self, device) -> "DecodeInputs":
         def mv(t):
@@ -94,7 +99,7 @@ class DecodeInputs:
         return DecodeInputs(mv(self.q_nope), mv(self.q_pe), mv(self.kv_cache), mv(self.block_table),
                             mv(self.seq_lens), mv(self.topk_indices), self.kv_dtype, self.out_dtype,
                             self.softmax_scale, self.q_scale, self.kv_scale, self.name, self.seed,
-                            dict(self.meta))
+                            dict(self.meta), self.max_len)
 
 
 # Workloads named by what they are.  Lengths: a list gives them outright, a
@@ -197,7 +202,7 @@ def make_inputs(B: int, H: int, T: int, seq_lens: Union[Sequence[int], Tuple[int
                         topk_indices=None if topk_indices is None else topk_indices.to(device),
                         kv_dtype=kv_dtype, out_dtype=out_dtype, softmax_scale=softmax_scale,
                         q_scale=q_scale, kv_scale=kv_scale, name=name, seed=seed,
-                        meta=dict(n_pages=n_pages, pool=pool))
+                        meta=dict(n_pages=n_pages, pool=pool), max_len=int(lens.max().item()) if B else 0)
 
 
 def workload(name: str, device="cpu", **overrides) -> DecodeInputs:

@@ -1,0 +1,155 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every symbol
+its header declares, sizes workspaces consistently, and rejects bad
+arguments before any launch (no compute call is made here)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from mla_paged_latent_03_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from mla_paged_latent_03_amd import build
+        build.build()
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("mla_decode", "mla_decode_fp8", "mla_sparse_decode", "mla_workspace_size", "mla_num_kv_splits",
+              "mla_status_string", "mla_num_kv_splits_baseline"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), "missing export %s" % name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    assert binding.status_string(0) == "ok"
+    assert binding.status_string(3) == "workspace too small"
+    assert binding.status_string(99) == "unknown status"
+
+
+def test_baseline_split_rule_matches_golden(lib):
+    with open(os.path.join(ROOT, "tests", "golden", "kv_splits_baseline.json")) as f:
+        for c in json.load(f)["cases"]:
+            assert binding.num_kv_splits_baseline(c["max_seq_len"], c["sm_count"]) == c["splits"], c
+    assert binding.num_kv_splits_baseline(-1, 256) == 0 and binding.num_kv_splits_baseline(100, 0) == 0
+
+
+@pytest.mark.parametrize("B,T,H,L,K,fp8", [
+    (2, 1, 16, 300, 0, False), (128, 1, 16, 8192, 0, False), (64, 4, 32, 80000, 0, True),
+    (32, 8, 128, 32768, 0, False), (64, 1, 128, 65536, 2048, False), (3, 2, 24, 5000, 300, False)])
+def test_workspace_matches_split_count(lib, B, T, H, L, K, fp8):
+    s = binding.num_kv_splits(B, T, H, L, K, fp8)
+    assert 1 <= s <= binding.MAX_KV_SPLITS
+    ws = binding.workspace_size(B, T, H, L, K, fp8, 0)
+    assert ws == (0 if s == 1 else B * T * H * s * 513 * 4)
+    for forced in (1, 2, 7):
+        ws = binding.workspace_size(B, T, H, L, K, fp8, forced)
+        assert ws == (0 if forced == 1 else B * T * H * forced * 513 * 4)
+
+
+def test_heuristic_fills_the_chip(lib):
+    # The 80k-token MTP-3 fp8 batch: 64 sequences x 1 row block -> 4 splits = 256 workgroups.
+    assert binding.num_kv_splits(64, 4, 32, 80000, 0, True) == 4
+    # One split whenever the splits' partials would cost more than they save.
+    assert binding.num_kv_splits(2, 1, 16, 300, 0, False) == 1
+    assert binding.num_kv_splits(64, 1, 128, 65536, 2048, False) == 1
+    # A top-k list longer than one workgroup's index table forces splits.
+    assert binding.num_kv_splits(1, 1, 16, 10000, 5000, False) >= 3
+
+
+def test_invalid_sizes_are_rejected(lib):
+    assert binding.num_kv_splits(1, 0, 16, 100) == 0
+    assert binding.num_kv_splits(1, 9, 16, 100) == 0
+    assert binding.num_kv_splits(1, 1, 0, 100) == 0
+    assert binding.workspace_size(1, 1, 16, 100, 0, False, 257) == 0
+    assert binding.workspace_size(1, 1, 16, 5000, 4096, False, 1) == 0   # K / splits above the index table
+
+
+FAKE = 0x10000   # aligned, never dereferenced: every call below fails validation first
+
+
+def _call_dense(lib, **kw):
+    a = dict(q_nope=FAKE, q_pe=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, B=2, T=1, H=16, NB=10, P=64, MB=5, msl=300,
+             scale=0.07, out=FAKE, odt=0, lse=FAKE, ws=None, wsb=0, splits=1)
+    a.update(kw)
+    return lib.mla_decode(a["q_nope"], a["q_pe"], a["kv"], a["bt"], a["sl"], a["B"], a["T"], a["H"], a["NB"],
+                          a["P"], a["MB"], a["msl"], a["scale"], a["out"], a["odt"], a["lse"], a["ws"], a["wsb"],
+                          a["splits"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(T=9), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(P=32), binding.MLA_ERR_UNSUPPORTED),
+    (dict(q_nope=None), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(bt=None), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(q_pe=FAKE + 8), binding.MLA_ERR_INVALID_ARGUMENT),     # misaligned
+    (dict(odt=7), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(splits=300), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(splits=-1), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(MB=0), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(splits=2, ws=FAKE, wsb=2 * 16 * 2 * 513 * 4 - 1), binding.MLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(splits=2, ws=None, wsb=0), binding.MLA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_dense_argument_errors(lib, kw, status):
+    assert _call_dense(lib, **kw) == status
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert _call_dense(lib, B=0, q_nope=None, out=None) == binding.MLA_OK
+
+
+def test_stage_one_only_needs_explicit_splits(lib):
+    assert _call_dense(lib, out=None, lse=None, splits=1) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _call_dense(lib, out=None, lse=None, splits=0) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _call_dense(lib, out=None, lse=FAKE, splits=2, ws=FAKE, wsb=1 << 20) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _call_dense(lib, out=None, lse=None, splits=2, ws=None, wsb=0) == binding.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_merge_partials_errors(lib):
+    f = lib.mla_merge_partials
+    assert f(FAKE, 10, 0, FAKE, 0, None, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 10, 257, FAKE, 0, None, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, -1, 2, FAKE, 0, None, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(None, 10, 2, FAKE, 0, None, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 10, 2, FAKE + 4, 0, None, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 10, 2, FAKE, 5, None, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(None, 0, 2, None, 0, None, None) == binding.MLA_OK
+
+
+def test_fp8_scale_errors(lib):
+    for qs, ks in ((0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0)):
+        st = lib.mla_decode_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, 16, 10, 64, 5, 300, 0.07, qs, ks, FAKE, 0,
+                                FAKE, None, 0, 1, None)
+        assert st == binding.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_sparse_errors(lib):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE]
+    tail = [2, 1, 16, 10, 64, 5, 300, 0.07, FAKE, 0, FAKE, None, 0, 1, None]
+    assert lib.mla_sparse_decode(*args, None, 64, *tail) == binding.MLA_ERR_INVALID_ARGUMENT   # no indices
+    assert lib.mla_sparse_decode(*args, FAKE, 0, *tail) == binding.MLA_ERR_INVALID_ARGUMENT    # K = 0
+    big = [2, 1, 16, 10, 64, 5, 300, 0.07, FAKE, 0, FAKE, None, 0, 1, None]
+    assert lib.mla_sparse_decode(*args, FAKE, 4096, *big) == binding.MLA_ERR_UNSUPPORTED      # 4096 / 1 split

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases compare every output element; they span several tiles, ragged
+tails, empty rows, forced split counts, every row-block width and both
+cache dtypes.  Full-size workloads run in the launch configuration the
+benchmark times and compare sampled rows the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mla_paged_latent_03_amd import binding, workloads as wl
+from parity import compare, oracle_rows, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(inp, num_kv_splits=0, what=""):
+    _say("[gpu] %s splits=%s B=%d T=%d H=%d kv=%s K=%d" % (what, num_kv_splits, inp.B, inp.T, inp.H, inp.kv_dtype,
+                                                           inp.K))
+    g = inp.to(DEV)
+    out, lse, _ = binding.decode(g, num_kv_splits=num_kv_splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_full(inp, num_kv_splits=0, what=""):
+    out, lse = run_case(inp, num_kv_splits, what)
+    ref_o, ref_l = oracle_rows(inp)
+    return compare(out, lse, ref_o, ref_l, inp.kv_dtype, what=what)
+
+
+# ------------------------------------------------------------------ tiny workload, every split count
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 7, 0])
+def test_tiny_workload_all_split_counts(splits):
+    inp = wl.workload("tiny_b2_h16_kv37-300", poison=True, extra_pages=3, extra_table_cols=2)
+    check_full(inp, splits, "tiny S=%d" % splits)
+
+
+def test_tiny_workload_split_results_agree():
+    # Runs with different split counts round P to bf16 against different
+    # reference maxima, so they agree to the bf16 budget, not bit for bit.
+    inp = wl.workload("tiny_b2_h16_kv37-300")
+    res = [run_case(inp, s, "tiny agree") for s in (1, 2, 5)]
+    for o, l in res[1:]:
+        assert torch.max(torch.abs(o - res[0][0])).item() < 1e-2
+        assert torch.max(torch.abs(l - res[0][1])).item() < 1e-5
+
+
+# ------------------------------------------------------------------ dense bf16 shapes
+
+@pytest.mark.parametrize("H,T,lens,splits", [
+    (16, 1, [1, 63, 64, 65, 700], 0),         # one-token, page-edge and ragged tails
+    (16, 1, [1, 63, 64, 65, 700], 3),
+    (32, 1, [129, 2000], 0),                  # one 32-row wave
+    (16, 4, [3, 4, 5, 130, 1000], 0),         # MTP: first queries of short sequences see nothing
+    (16, 4, [3, 4, 5, 130, 1000], 2),
+    (64, 2, [77, 1500], 2),                   # two waves per workgroup
+    (128, 1, [300, 1234], 0),                 # four waves per workgroup
+    (32, 8, [9, 640, 1111], 3),               # 256 rows: two row blocks
+    (128, 8, [100, 900], 0),                  # 1024 rows: eight row blocks
+    (24, 3, [50, 513], 0),                    # rows not a multiple of 32
+])
+def test_dense_bf16_shapes(H, T, lens, splits):
+    inp = wl.make_inputs(len(lens), H, T, lens, kv_dtype="bf16", out_dtype="f32", seed=7 + H + T, poison=True,
+                         extra_pages=2)
+    check_full(inp, splits, "dense bf16 H=%d T=%d" % (H, T))
+
+
+def test_dense_bf16_out_bf16_and_no_lse():
+    inp = wl.make_inputs(2, 16, 2, [90, 400], kv_dtype="bf16", out_dtype="bf16", seed=3)
+    g = inp.to(DEV)
+    out = torch.empty((2, 2, 16, 512), device=DEV, dtype=torch.bfloat16)
+    _say("[gpu] dense bf16 no-lse")
+    binding.mla_decode(g.q_nope, g.q_pe, g.kv_cache, g.block_table, g.seq_lens, g.max_seq_len, g.softmax_scale,
+                       out, None, None, 1)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_rows(inp)
+    compare(out, torch.tensor(ref_l), ref_o, ref_l, "bf16", what="no lse")
+
+
+def test_empty_sequence_gives_zero_and_neg_inf():
+    inp = wl.make_inputs(3, 16, 1, [0, 1, 100], kv_dtype="bf16", out_dtype="f32", seed=4)
+    for s in (1, 2):
+        out, lse = run_case(inp, s, "empty seq")
+        assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+        check_full(inp, s, "empty seq")
+
+
+def test_single_token_closed_form_is_exact():
+    inp = wl.make_inputs(2, 32, 1, [1, 1], kv_dtype="bf16", out_dtype="f32", seed=5)
+    out, lse = run_case(inp, 1, "single token")
+    kv = inp.kv_cache.to(torch.float32)
+    for b in range(2):
+        c0 = kv[int(inp.block_table[b, 0]), 0, :512]
+        assert torch.equal(out[b, 0].cpu(), c0.expand(32, 512)), "out must be the token's latent exactly"
+        s0 = inp.softmax_scale * (inp.q_nope[b, 0].double() @ kv[int(inp.block_table[b, 0]), 0, :512].double() +
+                                  inp.q_pe[b, 0].double() @ kv[int(inp.block_table[b, 0]), 0, 512:].double())
+        assert torch.allclose(lse[b, 0].cpu().double(), s0, rtol=1e-5, atol=1e-5)
+
+
+def test_page_permutation_bit_identical():
+    inp = wl.make_inputs(2, 16, 2, [333, 1000], kv_dtype="bf16", out_dtype="f32", seed=6)
+    o1, l1 = run_case(inp, 2, "perm a")
+    perm = torch.randperm(inp.NB, generator=torch.Generator().manual_seed(1))
+    inv = torch.argsort(perm)
+    inp2 = wl.DecodeInputs(inp.q_nope, inp.q_pe, inp.kv_cache[perm].contiguous(),
+                           torch.where(inp.block_table >= 0, inv[inp.block_table.clamp(min=0)].to(torch.int32),
+                                       inp.block_table), inp.seq_lens, None, "bf16", "f32", inp.softmax_scale)
+    o2, l2 = run_case(inp2, 2, "perm b")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_causal_row_equals_single_query_call():
+    T = 4
+    inp = wl.make_inputs(2, 16, T, [70, 515], kv_dtype="bf16", out_dtype="f32", seed=8)
+    o, l = run_case(inp, 0, "causal T=4")
+    for t in range(T):
+        sub = wl.DecodeInputs(inp.q_nope[:, t:t + 1].contiguous(), inp.q_pe[:, t:t + 1].contiguous(), inp.kv_cache,
+                              inp.block_table, (inp.seq_lens - T + t + 1).to(torch.int32), None, "bf16", "f32",
+                              inp.softmax_scale)
+        o1, l1 = run_case(sub, 0, "causal t=%d" % t)
+        assert torch.max(torch.abs(o[:, t] - o1[:, 0])).item() < 1e-5
+        assert torch.max(torch.abs(l[:, t] - l1[:, 0])).item() < 1e-5
+
+
+def test_scale_is_read_every_call():
+    inp = wl.make_inputs(2, 16, 1, [200, 300], kv_dtype="bf16", out_dtype="f32", seed=9)
+    for sc in (inp.softmax_scale, 0.5, 1.0 / 64):
+        inp.softmax_scale = sc
+        check_full(inp, 0, "scale %.4f" % sc)
+
+
+# ------------------------------------------------------------------ fp8
+
+@pytest.mark.parametrize("H,T,lens,splits", [
+    (32, 4, [4, 100, 300, 700], 0),
+    (32, 4, [4, 100, 300, 700], 3),
+    (16, 1, [1, 64, 129], 2),
+    (128, 2, [257, 1000], 0),
+])
+def test_dense_fp8_shapes(H, T, lens, splits):
+    inp = wl.make_inputs(len(lens), H, T, lens, kv_dtype="fp8", out_dtype="f32", seed=11 + H, poison=True,
+                         extra_pages=1)
+    check_full(inp, splits, "fp8 H=%d T=%d" % (H, T))
+
+
+def test_fp8_scales_are_read_every_call():
+    inp = wl.make_inputs(2, 32, 4, [500, 900], kv_dtype="fp8", out_dtype="f32", seed=12)
+    for ks in (inp.kv_scale, inp.kv_scale * 4.0, inp.kv_scale * 0.25):
+        inp.kv_scale = ks
+        check_full(inp, 0, "fp8 kv_scale %.3g" % ks)
+
+
+# ------------------------------------------------------------------ sparse
+
+@pytest.mark.parametrize("H,T,lens,K,splits", [
+    (16, 1, [100, 3000], 256, 0),      # first sequence shorter than K: -1 padding
+    (16, 1, [100, 3000], 256, 2),
+    (128, 1, [5000, 70], 512, 0),
+    (64, 2, [900, 2500], 192, 0),      # MTP with per-token index lists
+    (32, 1, [4100], 4096, 0),          # K above one workgroup's index table: forced splits
+])
+def test_sparse_shapes(H, T, lens, K, splits):
+    inp = wl.make_inputs(len(lens), H, T, lens, kv_dtype="bf16", out_dtype="f32", topk=K, seed=13 + H, poison=True)
+    check_full(inp, splits, "sparse H=%d K=%d" % (H, K))
+
+
+def test_sparse_out_of_range_and_duplicate_indices():
+    inp = wl.make_inputs(2, 16, 1, [300, 300], kv_dtype="bf16", out_dtype="f32", topk=128, seed=14)
+    idx = inp.topk_indices.clone()
+    idx[0, 0, :10] = 7                      # duplicates
+    idx[0, 0, 10:20] = 300                  # == L: out of range
+    idx[1, 0, :5] = -5
+    idx[1, 0, 5:9] = 1 << 30
+    inp.topk_indices = idx
+    check_full(inp, 0, "sparse odd indices")
+
+
+def test_sparse_index_probe_histogram_exact():
+    """q = 0 and latent c_j = e_(j mod 512): n * out is the exact histogram."""
+    L, K = 2000, 1024
+    inp = wl.make_inputs(1, 16, 1, [L], kv_dtype="bf16", out_dtype="f32", topk=K, seed=15)
+    inp.q_nope.zero_()
+    inp.q_pe.zero_()
+    kv = torch.zeros_like(inp.kv_cache, dtype=torch.float32)
+    for j in range(L):
+        kv[int(inp.block_table[0, j // 64]), j % 64, j % 512] = 1.0
+    inp.kv_cache = kv.to(torch.bfloat16)
+    idx = inp.topk_indices
+    idx[0, 0, :50] = 3                      # duplicates count
+    idx[0, 0, 50:60] = -1
+    out, lse = run_case(inp, 0, "index probe")
+    sel = idx[0, 0][(idx[0, 0] >= 0) & (idx[0, 0] < L)]
+    n = sel.numel()
+    hist = torch.bincount(sel.long() % 512, minlength=512)
+    got = torch.round(out[0, 0].cpu().double() * n).long()
+    for h in range(16):
+        assert torch.equal(got[h], hist), "histogram mismatch in head %d" % h
+    assert torch.allclose(lse.cpu().double(), torch.full_like(lse.cpu().double(), math.log(n)), atol=1e-6)
+
+
+def test_sparse_all_positions_equals_dense():
+    L, K = 300, 512
+    inp = wl.make_inputs(1, 32, 1, [L], kv_dtype="bf16", out_dtype="f32", topk=K, seed=16)
+    o_s, l_s = run_case(inp, 0, "sparse all positions")
+    dense = wl.DecodeInputs(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, None, "bf16", "f32",
+                            inp.softmax_scale)
+    o_d, l_d = run_case(dense, 0, "dense twin")
+    # Same tokens in another order: equal up to bf16 rounding of P.
+    assert torch.max(torch.abs(o_s - o_d)).item() < 1e-2
+    assert torch.max(torch.abs(l_s - l_d)).item() < 1e-5
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_hip_graph_replay_matches_eager():
+    inp = wl.make_inputs(4, 32, 4, [100, 800, 2000, 64], kv_dtype="fp8", out_dtype="bf16", seed=17).to(DEV)
+    _say("[gpu] graph capture")
+    eager_o, eager_l, ws = binding.decode(inp, num_kv_splits=3)
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager_o)
+    lse = torch.empty_like(eager_l)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        binding.decode(inp, num_kv_splits=3, out=out, lse=lse, workspace=ws)   # warm the stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            binding.decode(inp, num_kv_splits=3, out=out, lse=lse, workspace=ws, stream=s)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), "replay %d differs" % rep
+        binding.decode(inp, num_kv_splits=1)   # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled rows)
+
+FULL = ["r1_b128_h16_kv1k-8k_bf16", "mtp3_b64_h32_kv80k_fp8", "mtp7_b32_h128_kv16k-32k_bf16",
+        "sparse_b64_h128_kv64k_top2048_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload_sampled_rows(name):
+    _say("[gpu] full-size %s: drawing inputs" % name)
+    inp = wl.workload(name, device=DEV)
+    out, lse, _ = binding.decode(inp)          # default (library-chosen) launch configuration
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all().item()
+    assert torch.isfinite(lse).all().item()
+    n_total = inp.B * inp.T * inp.H
+    rows = sample_rows(n_total, 48, seed=sum(name.encode()))
+    cpu = inp.to("cpu")
+    _say("[gpu] full-size %s: oracle on %d rows" % (name, rows.size))
+    ref_o, ref_l = oracle_rows(cpu, rows=rows)
+    compare(out, lse, ref_o, ref_l, inp.kv_dtype, rows=rows, what=name)
+
+
+# ------------------------------------------------------------------ two-stage form
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_stage_one_then_merge_equals_one_call(kv_dtype):
+    inp = wl.make_inputs(3, 32, 2, [100, 700, 1500], kv_dtype=kv_dtype, out_dtype="f32", seed=21).to(DEV)
+    _say("[gpu] two-stage %s" % kv_dtype)
+    ref_o, ref_l, ws = binding.decode(inp, num_kv_splits=3)
+    out = torch.empty_like(ref_o)
+    lse = torch.empty_like(ref_l)
+    ws.fill_(float("nan"))
+    if kv_dtype == "fp8":
+        binding.mla_decode_fp8(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, inp.max_seq_len,
+                               inp.softmax_scale, inp.q_scale, inp.kv_scale, None, None, ws, 3)
+    else:
+        binding.mla_decode(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, inp.max_seq_len,
+                           inp.softmax_scale, None, None, ws, 3)
+    binding.mla_merge_partials(ws, inp.B * inp.T * inp.H, 3, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
