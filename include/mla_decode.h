@@ -40,9 +40,9 @@
  *
  * Conventions shared by every entry point:
  *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
- *    row-major, on the current HIP device.  The library allocates nothing,
- *    keeps no per-call state and caches only the device's compute-unit
- *    count.
+ *    row-major, on the current HIP device.  The library allocates nothing
+ *    and keeps no state between calls; its launch plan assumes the 256
+ *    compute units of an MI355X.
  *  - Calls enqueue on `stream` (a hipStream_t; NULL = the null stream) and
  *    return without synchronizing; they are safe to capture in a HIP graph.
  *  - Scales are read on every call and never cached (the pages record a
@@ -53,7 +53,10 @@
  *  - Errors the host can see are returned BEFORE any launch, and nothing is
  *    enqueued: bad dims, T outside [1, 8], block_size != 64, a NULL required
  *    pointer, num_kv_splits outside [0, MLA_MAX_KV_SPLITS], a workspace
- *    smaller than mla_workspace_size().  A failed launch returns MLA_ERR_HIP.
+ *    smaller than mla_workspace_size().  A split may cover at most 2048
+ *    pages (dense) or 2048 top-k entries (sparse); an explicit num_kv_splits
+ *    that violates this returns MLA_ERR_UNSUPPORTED (the library's own choice
+ *    never does).  A failed launch returns MLA_ERR_HIP.
  *  - Device data is not validated on the host.  In the kernels, seq_lens are
  *    clamped to [0, max_blocks_per_seq * 64], page numbers outside
  *    [0, num_blocks) read as zero vectors, and block-table slots past a
@@ -110,6 +113,14 @@ const char* mla_status_string(mla_status_t status);
  */
 int mla_num_kv_splits(int batch, int q_len, int num_heads, int max_seq_len, int topk,
                       int kv_fp8);
+
+/*
+ * Waves per workgroup (1, 2 or 4; each wave owns 32 query rows) that a call
+ * with these arguments launches.  Follows from the shape alone, whatever
+ * num_kv_splits is; lets tests and tuning tell which kernel variant a shape
+ * runs.  Returns 0 on invalid arguments.
+ */
+int mla_launch_waves(int batch, int q_len, int num_heads, int max_seq_len, int topk, int kv_fp8);
 
 /*
  * Workspace bytes a call needs: batch * q_len * num_heads * splits * 513 * 4,

@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
 MLA_OK, MLA_ERR_INVALID_ARGUMENT, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP = range(5)
 MLA_OUT_BF16, MLA_OUT_F32 = 0, 1
 MAX_KV_SPLITS = 256
-EXPORTS = ("mla_status_string", "mla_num_kv_splits", "mla_workspace_size", "mla_num_kv_splits_baseline",
-           "mla_decode", "mla_decode_fp8", "mla_sparse_decode", "mla_merge_partials")
+EXPORTS = ("mla_status_string", "mla_num_kv_splits", "mla_launch_waves", "mla_workspace_size",
+           "mla_num_kv_splits_baseline", "mla_decode", "mla_decode_fp8", "mla_sparse_decode", "mla_merge_partials")
 
 _lib = None
 
@@ -44,6 +44,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_status_string.argtypes = [c_int]
     lib.mla_num_kv_splits.restype = c_int
     lib.mla_num_kv_splits.argtypes = [c_int] * 6
+    lib.mla_launch_waves.restype = c_int
+    lib.mla_launch_waves.argtypes = [c_int] * 6
     lib.mla_workspace_size.restype = c_size
     lib.mla_workspace_size.argtypes = [c_int] * 7
     lib.mla_num_kv_splits_baseline.restype = c_int
@@ -67,6 +69,11 @@ def status_string(status: int) -> str:
 
 def num_kv_splits(batch, q_len, num_heads, max_seq_len, topk=0, kv_fp8=False) -> int:
     return load().mla_num_kv_splits(batch, q_len, num_heads, max_seq_len, topk, int(bool(kv_fp8)))
+
+
+def launch_waves(batch, q_len, num_heads, max_seq_len, topk=0, kv_fp8=False) -> int:
+    """Waves per workgroup (1, 2 or 4) the library launches for this shape."""
+    return load().mla_launch_waves(batch, q_len, num_heads, max_seq_len, topk, int(bool(kv_fp8)))
 
 
 def workspace_size(batch, q_len, num_heads, max_seq_len, topk=0, kv_fp8=False, num_kv_splits=0) -> int:

@@ -13,6 +13,7 @@ namespace {
 
 using mla::kNumCUs;
 using mla::kPartialWidth;
+using mla::kDensePagesMax;
 using mla::kSparseChunkMax;
 
 struct Plan {
@@ -56,7 +57,9 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
   const int64_t min_tokens_per_split = (int64_t)std::ceil(16.0 * part_bytes / kv_token_bytes);
   int s_ovh = (int)(tokens / (min_tokens_per_split > 0 ? min_tokens_per_split : 1));
   if (s_ovh < 1) s_ovh = 1;
-  const int s_min = sparse ? ceil_div(topk, kSparseChunkMax) : 1;   // LDS index table capacity
+  // A split's index / page table lives in LDS, which bounds its length.
+  const int s_min = sparse ? ceil_div(topk, kSparseChunkMax)
+                           : ceil_div(ceil_div(max_seq_len, MLA_BLOCK_SIZE), kDensePagesMax);
 
   int rg = rg_for_rows(rows_blk);
   int S = 1;
@@ -74,7 +77,7 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
   if (S > MLA_MAX_KV_SPLITS) S = MLA_MAX_KV_SPLITS;
   if (req_splits > 0) S = req_splits;
   if (S < s_min) {
-    if (req_splits > 0) return false;   // K / splits would exceed the index table
+    if (req_splits > 0) return false;   // the split would exceed the LDS table
     S = s_min;
   }
   p.rg = rg;
@@ -90,6 +93,7 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
     p.n_rb = ceil_div(p.R, rb_rows);
     const int max_pages = ceil_div(max_seq_len, MLA_BLOCK_SIZE);
     p.chunk = max_pages > 0 ? ceil_div(max_pages, S) : 1;
+    if (p.chunk > kDensePagesMax) return false;
   }
   p.S = S;
   p.ws_bytes = S > 1 ? (size_t)B * p.R * S * kPartialWidth * sizeof(float) : 0;
@@ -126,8 +130,7 @@ mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv_cache) || !aligned16(out))
     return MLA_ERR_INVALID_ARGUMENT;
   Plan pl;
-  if (!make_plan(B, T, H, max_seq_len, sparse ? topk : 0, fp8, num_kv_splits, &pl))
-    return sparse ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARGUMENT;
+  if (!make_plan(B, T, H, max_seq_len, sparse ? topk : 0, fp8, num_kv_splits, &pl)) return MLA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0) {
     if (workspace_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
     if (!workspace || !aligned16(workspace)) return MLA_ERR_INVALID_ARGUMENT;
@@ -197,6 +200,12 @@ int mla_num_kv_splits(int batch, int q_len, int num_heads, int max_seq_len, int 
   Plan pl;
   if (!make_plan(batch, q_len, num_heads, max_seq_len, topk, kv_fp8 != 0, 0, &pl)) return 0;
   return pl.S;
+}
+
+int mla_launch_waves(int batch, int q_len, int num_heads, int max_seq_len, int topk, int kv_fp8) {
+  Plan pl;
+  if (!make_plan(batch, q_len, num_heads, max_seq_len, topk, kv_fp8 != 0, 0, &pl)) return 0;
+  return pl.rg;
 }
 
 size_t mla_workspace_size(int batch, int q_len, int num_heads, int max_seq_len, int topk, int kv_fp8,

@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mla_decode_internal.h"
 
 namespace mla {
@@ -59,6 +61,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;  // running-max sentinel: finite, below any logit
+constexpr int kE4m3OnesX4 = 0x38383838;  // four e4m3 1.0 bytes
 
 // A zero token row: DMA source for tokens past the end of a sequence, padded
 // or out-of-range top-k entries and out-of-range page numbers, so that no
@@ -119,12 +122,18 @@ __device__ inline void wait_tiles_after(int remaining) {
   wait_vmcnt<0>();
 }
 
-// Combine the two halves of a wave (lanes l and l ^ 32 hold the same row).
-// (v_permlane32_swap of a value with itself gets folded to a no-op by the
-// compiler, so the exchange goes through ds_bpermute.)
-__device__ inline float max_across_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// Combine the two halves of a wave (lanes l and l ^ 32 hold the same row)
+// with v_permlane32_swap.  Issued from inline asm: the builtin applied to
+// one value twice gets folded away by the compiler.
+__device__ inline float other_half(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  // a = [x_lo, x_lo], b = [x_hi, x_hi]: each lane takes the half it lacks.
+  return (__lane_id() < 32) ? b : a;
+}
+__device__ inline float max_across_halves(float x) { return fmaxf(x, other_half(x)); }
 
-__device__ inline float sum_across_halves(float x) { return x + __shfl_xor(x, 32); }
+__device__ inline float sum_across_halves(float x) { return x + other_half(x); }
 
 // 16-byte global -> LDS DMA: lane i writes LDS bytes [m0 + 16 i, m0 + 16 i + 16).
 // Issued from inline asm so the compiler does not treat it as an LDS store
@@ -132,6 +141,37 @@ __device__ inline float sum_across_halves(float x) { return x + __shfl_xor(x, 32
 // cannot prove disjoint); completion is tracked explicitly with vmcnt.
 __device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_byte_addr) : "memory");
+}
+
+// MFMAs whose accumulator must stay in VGPRs.  The output accumulator O
+// fills all 256 AGPRs; the compiler would otherwise give the score and
+// row-sum accumulators AGPRs too and shuttle two O tiles through VGPRs on
+// every tile.  Being inline asm, these carry their own hazard padding: three
+// wait states before the product (a VALU write of an operand needs two), and
+// callers end a chain with mfma_drain(acc) before any VALU reads the result
+// (an XDL result needs about 18).  Back-to-back products on one accumulator
+// need no padding (the compiler emits none for such chains either).
+__device__ inline void mfma_f8_first(f32x16_t& acc, const i32x8_t& a, const i32x8_t& b, int sa, int sb) {
+  asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+               : "=&v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+__device__ inline void mfma_f8_acc(f32x16_t& acc, const i32x8_t& a, const i32x8_t& b, int sa, int sb) {
+  asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+__device__ inline void mfma_bf16_first(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_bf16_acc(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// 24 wait states after the last product of a chain.  The accumulators are
+// in/out operands: code that reads them then depends on this statement and
+// cannot be scheduled above the padding (with no operands the compiler is
+// free to hoist such reads above it, right behind the product).
+__device__ inline void mfma_drain(f32x16_t& a) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a)); }
+__device__ inline void mfma_drain(f32x16_t& a, f32x16_t& b) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
 }
 
 // ---------------------------------------------------------------------------
@@ -144,6 +184,10 @@ __device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
 //            (a second fp8 product), so each softmax weight is carried to
 //            about 2^-8 instead of 2^-4; chosen for short work units, where
 //            a few tokens can dominate a row
+//
+// With four waves (RG = 4) the tile loop is software-pipelined: the QK
+// products of tile i+1 are issued interleaved with the PV products of tile
+// i, so the two dependent QK accumulator chains never stall the matrix pipe.
 template <bool FP8, bool SPARSE, int RG, int NS, bool RESID>
 __global__ void __launch_bounds__(64 * RG) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_partial_kernel(const PartialParams p) {
@@ -151,10 +195,15 @@ mla_partial_kernel(const PartialParams p) {
   constexpr int NI = kInstrPerTile / RG;          // DMA instructions per wave per tile
   constexpr int NPRE = NI <= 18 ? NI : K::kPeriodInstr;
   static_assert(NI % NPRE == 0, "DMA offset period");
-  constexpr int kSparseCap = SPARSE ? kSparseChunkMax : 0;
+  constexpr bool PIPE = RG == 4;
+  static_assert(!PIPE || NS >= 3, "the pipelined loop keeps two tiles resident");
+  constexpr int kTableCap = SPARSE ? kSparseChunkMax : kDensePagesMax;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kTileBytes + kSparseCap * 4 + 16];
+  // LDS: [ring of NS tiles][unit table: int32 x kTableCap][redo flag]
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kTileBytes + kTableCap * 4 + 16];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
+  LDS_AS int* table = (LDS_AS int*)(lds + NS * kTileBytes);
+  LDS_AS int* redo_flag = table + kTableCap;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -191,7 +240,7 @@ mla_partial_kernel(const PartialParams p) {
   const int64_t qrow = (int64_t)b * p.R + row;
 
   // ---- token range of the unit
-  int n_tiles, tok_begin = 0, idx_begin = 0, idx_count = 0;
+  int n_tiles, tok_begin = 0, idx_begin = 0, idx_count = 0, page0 = 0, n_unit_pages = 0;
   if (SPARSE) {
     idx_begin = split * p.chunk;
     idx_count = min(p.chunk, p.K - idx_begin);
@@ -199,19 +248,19 @@ mla_partial_kernel(const PartialParams p) {
     n_tiles = (idx_count + K::kTileTok - 1) / K::kTileTok;
   } else {
     const int n_pages = (L + 63) >> 6;
-    const int p0 = split * p.chunk;
-    const int p1 = min(p0 + p.chunk, n_pages);
-    tok_begin = p0 * 64;
-    const int tok_end = p1 > p0 ? min(p1 * 64, L) : tok_begin;
+    page0 = split * p.chunk;
+    const int p1 = min(page0 + p.chunk, n_pages);
+    n_unit_pages = p1 > page0 ? p1 - page0 : 0;
+    tok_begin = page0 * 64;
+    const int tok_end = n_unit_pages > 0 ? min(p1 * 64, L) : tok_begin;
     n_tiles = (tok_end - tok_begin + K::kTileTok - 1) / K::kTileTok;
     if (n_tiles < 0) n_tiles = 0;
   }
-  // Highest position any row of this sequence may see (dense causal limit of
-  // the last draft token); tiles fully below the first row's limit skip masks.
   const int n_vis = L - p.T + t_row + 1;  // dense: visible tokens of this row
 
-  // ---- sparse: physical row table for this unit's index range, in LDS
-  LDS_AS int* sp_rows = (LDS_AS int*)(lds + NS * kTileBytes);
+  // ---- unit table in LDS.  Dense: physical page of each page of the unit
+  // (-1 if out of range).  Sparse: physical token row of each index (-1 for
+  // padding / out-of-range entries).
   if (SPARSE) {
     const int32_t* idx = p.topk + ((int64_t)b * p.T + (rb / p.n_hb)) * p.K + idx_begin;
     const int n_ent = n_tiles * K::kTileTok;
@@ -224,10 +273,16 @@ mla_partial_kernel(const PartialParams p) {
           if (pg >= 0 && pg < p.NB) phys = pg * 64 + (j & 63);
         }
       }
-      sp_rows[e] = phys;
+      table[e] = phys;
     }
-    __syncthreads();
+  } else {
+    const int32_t* bt = p.block_table + (int64_t)b * p.MB + page0;
+    for (int e = threadIdx.x; e < n_unit_pages; e += 64 * RG) {
+      const int pg = bt[e];
+      table[e] = (pg >= 0 && pg < p.NB) ? pg : -1;
+    }
   }
+  __syncthreads();
 
   // ---- query operand in registers (B side: lane holds row l32, a K slice)
   // bf16: step k covers features 16k .. 16k+15; lane half h holds 8 of them.
@@ -278,7 +333,7 @@ mla_partial_kernel(const PartialParams p) {
   auto issue_tile = [&](int i, int slot) {
     const uint32_t dst = (uint32_t)(uintptr_t)(lds + slot * kTileBytes + wave * NI * 1024);
     if (SPARSE) {
-      LDS_AS const int* rows_tab = sp_rows + i * K::kTileTok;
+      LDS_AS const int* rows_tab = table + i * K::kTileTok;
 #pragma unroll
       for (int j = 0; j < NI; j++) {
         const int off = dma_off[j % NPRE] + (j / NPRE) * kPeriodBytes;
@@ -290,10 +345,9 @@ mla_partial_kernel(const PartialParams p) {
       }
     } else {
       const int tok0 = tok_begin + i * K::kTileTok;     // first token of the tile
-      const int pg = ((const CONST_AS int32_t*)p.block_table)[(int64_t)b * p.MB + (tok0 >> 6)];
-      const bool page_ok = pg >= 0 && pg < p.NB;
-      const uint8_t* base = p.kv + ((int64_t)(page_ok ? pg : 0) * 64 + (tok0 & 63)) * K::kRowBytes;
-      const int n_valid = page_ok ? min(K::kTileTok, L - tok0) : 0;
+      const int pg = table[(tok0 >> 6) - page0];        // same address in every lane: LDS broadcast
+      const uint8_t* base = p.kv + ((int64_t)(pg >= 0 ? pg : 0) * 64 + (tok0 & 63)) * K::kRowBytes;
+      const int n_valid = pg >= 0 ? min(K::kTileTok, L - tok0) : 0;
       if (n_valid == K::kTileTok) {
 #pragma unroll
         for (int j = 0; j < NI; j++) {
@@ -350,6 +404,44 @@ mla_partial_kernel(const PartialParams p) {
     }
   }
 
+  // ---- operand loaders
+  // QK product n: fp8 -> step n/2 of token block n%2; bf16 -> step n.
+  constexpr int NQK = FP8 ? 2 * K::kQkSteps : K::kQkSteps;     // 18 | 36
+  constexpr int NPV = FP8 ? 16 : 32;                            // fp8: block fb; bf16: 2 fb + kk
+  typedef typename std::conditional<FP8, i32x8_t, bf16x8_t>::type opnd_t;
+  auto ld_qk = [&](const LDS_AS uint8_t* tile, int n) -> opnd_t {
+    if constexpr (FP8) {
+      const LDS_AS uint8_t* base = tile + (n & 1) * 32 * K::kRowBytes + 64 * (n >> 1);
+      const i32x4_t lo = *(const LDS_AS i32x4_t*)(base + a_off[0]);
+      const i32x4_t hi = *(const LDS_AS i32x4_t*)(base + a_off[1]);
+      return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return __builtin_bit_cast(bf16x8_t, *(const LDS_AS i32x4_t*)(tile + a_off[n & 3] + 128 * (n >> 2)));
+    }
+  };
+  auto ld_pv = [&](const LDS_AS uint8_t* tile, int n) -> opnd_t {
+    if constexpr (FP8) {
+      i32x8_t a;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const i32x2_t d =
+            __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2_t*)(tile + v_off[r][n & 1] + 32 * n));
+        a[2 * r] = d[0];
+        a[2 * r + 1] = d[1];
+      }
+      return a;
+    } else {
+      const int fb = n >> 1, kk = n & 1;
+      const i16x4_t d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4_t*)(tile + v_off[0][fb & 1] + 64 * fb + 16 * kk * K::kRowBytes));
+      const i16x4_t d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4_t*)(tile + v_off[1][fb & 1] + 64 * fb + 16 * kk * K::kRowBytes));
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const i16x8_t cat = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      return __builtin_bit_cast(bf16x8_t, cat);
+    }
+  };
+
   // ---- accumulators and softmax state (per lane: row l32, its half of tokens)
   //
   // Each row accumulates O and l relative to a fixed reference m_ref (log2
@@ -359,194 +451,282 @@ mla_partial_kernel(const PartialParams p) {
   // maximum ever exceeds m_ref by more than 2^64 (fp32 headroom for O) is the
   // whole unit run a second time with m_ref = that row's true maximum.
   f32x16_t oacc[16];
+  f32x16_t lsum;                   // ones x P^T: row sum of the rounded weights (normalizes out)
   float m_ref = kNegBig;
-  float m_seen = -INFINITY;        // running row maximum, for the second pass
-  float l_q = 0.f;                 // row sum of the rounded weights (normalizes out)
-  float l_f = 0.f;                 // row sum of the unrounded weights (gives lse)
+  float m_seen = -INFINITY;        // running lane maximum, for the second pass
+  float l_f = 0.f;                 // this half's sum of the unrounded weights (gives lse)
   const float c_qk = p.qk_scale;   // softmax_scale * log2(e) [* q_scale * kv_scale]
-  LDS_AS int* redo_flag = (LDS_AS int*)(lds + NS * kTileBytes + kSparseCap * 4);
+  const int e8m0_one = 127;        // E8M0 scale 2^0 (a VGPR operand of the inline-asm products)
 
+  // Softmax output of one tile, consumed by its PV products.
+  struct PTile {
+    i32x8_t pb, pbl;    // fp8: e4m3 weights (and residual); bf16: two bf16x8 packed
+    int sc, scl;        // fp8: E8M0 scales of pb / pbl
+  };
+
+  // QK product n on accumulator sacc (VGPR chain).
+  auto qk_mfma = [&](f32x16_t (&sacc)[K::kTokBlocks], int n, const opnd_t& a) {
+    if constexpr (FP8) {
+      const int k = n >> 1, tb = n & 1;
+      const i32x8_t bq = {qreg[8 * k], qreg[8 * k + 1], qreg[8 * k + 2], qreg[8 * k + 3],
+                          qreg[8 * k + 4], qreg[8 * k + 5], qreg[8 * k + 6], qreg[8 * k + 7]};
+      if (k == 0) mfma_f8_first(sacc[tb], a, bq, e8m0_one, e8m0_one);
+      else mfma_f8_acc(sacc[tb], a, bq, e8m0_one, e8m0_one);
+    } else {
+      const i32x4_t bq = {qreg[4 * n], qreg[4 * n + 1], qreg[4 * n + 2], qreg[4 * n + 3]};
+      if (n == 0) mfma_bf16_first(sacc[0], a, __builtin_bit_cast(bf16x8_t, bq));
+      else mfma_bf16_acc(sacc[0], a, __builtin_bit_cast(bf16x8_t, bq));
+    }
+  };
+  // PV product n of a tile with softmax output pt.
+  auto pv_mfma = [&](int n, const opnd_t& a, const PTile& pt) {
+    if constexpr (FP8) {
+      oacc[n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pt.pb, oacc[n], 0, 0, 0, 127, 0, pt.sc);
+      if constexpr (RESID)
+        oacc[n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pt.pbl, oacc[n], 0, 0, 0, 127, 0, pt.scl);
+    } else {
+      const i32x4_t half = n & 1 ? i32x4_t{pt.pb[4], pt.pb[5], pt.pb[6], pt.pb[7]}
+                                 : i32x4_t{pt.pb[0], pt.pb[1], pt.pb[2], pt.pb[3]};
+      oacc[n >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, half), oacc[n >> 1], 0,
+                                                             0, 0);
+    }
+  };
+  auto row_sum_mfma = [&](const PTile& pt) {
+    // The all-ones operand is rebuilt at each use rather than held live.
+    const i32x8_t ones8 = {kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4,
+                           kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4};
+    const bf16x8_t ones16 = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                             (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+    if constexpr (FP8) {
+      mfma_f8_acc(lsum, ones8, pt.pb, e8m0_one, pt.sc);
+      if constexpr (RESID) mfma_f8_acc(lsum, ones8, pt.pbl, e8m0_one, pt.scl);
+    } else {
+      mfma_bf16_acc(lsum, ones16, __builtin_bit_cast(bf16x8_t, i32x4_t{pt.pb[0], pt.pb[1], pt.pb[2], pt.pb[3]}));
+      mfma_bf16_acc(lsum, ones16, __builtin_bit_cast(bf16x8_t, i32x4_t{pt.pb[4], pt.pb[5], pt.pb[6], pt.pb[7]}));
+    }
+  };
+
+  // Padding after a tile's QK chain, tied to its score accumulators.
+  auto drain_scores = [&](f32x16_t (&sacc)[K::kTokBlocks]) {
+    if constexpr (K::kTokBlocks == 2) mfma_drain(sacc[0], sacc[1]);
+    else mfma_drain(sacc[0]);
+  };
+
+  // Mask + softmax of tile i from its scores; updates the row state.
+  auto softmax = [&](f32x16_t (&sacc)[K::kTokBlocks], int i, bool& jumped) -> PTile {
+    // Register v of token block tb holds token 32*tb + 8*(v/4) + 4*h + v%4.
+    // The masks compare that compile-time offset (without the 4*h) against
+    // one per-lane quantity, so no per-register index lives in a VGPR.
+    if (SPARSE) {
+      const int phys = lane < K::kTileTok ? table[i * K::kTileTok + lane] : 0;
+      const uint64_t valid = __builtin_amdgcn_ballot_w64(phys >= 0) | (K::kTileTok == 64 ? 0ull : ~0ull << 32);
+      const uint64_t mine = valid >> (4 * h);   // branch-free, as below
+#pragma unroll
+      for (int tb = 0; tb < K::kTokBlocks; tb++)
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+          sacc[tb][v] = (mine >> (32 * tb + 8 * (v >> 2) + (v & 3))) & 1 ? sacc[tb][v] : -INFINITY;
+    } else {
+      // Branch-free: a branch here splits the pipelined loop body and costs
+      // far more registers than these selects.
+      const int lim = n_vis - (tok_begin + i * K::kTileTok) - 4 * h;   // offsets at or past lim are masked
+#pragma unroll
+      for (int tb = 0; tb < K::kTokBlocks; tb++)
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+          sacc[tb][v] = 32 * tb + 8 * (v >> 2) + (v & 3) < lim ? sacc[tb][v] : -INFINITY;
+    }
+    float ml = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < K::kTokBlocks; tb++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) ml = fmaxf(ml, sacc[tb][v]);
+    ml *= c_qk;                          // this lane's maximum, scaled (-inf if all masked)
+    m_seen = fmaxf(m_seen, ml);
+    // A jump is measured against a reference already set by an earlier tile.
+    jumped |= m_ref != kNegBig && ml > m_ref + 64.f;
+    PTile pt;
+    if constexpr (FP8) {
+      // P' = 2^(x - mi + 8) in [0, 256] -> e4m3, with mi the integer ceiling
+      // of the row's tile maximum; the PV MFMA multiplies it by 2^(mi - m_ref)
+      // through the E8M0 scale of its P operand.  (The scale must be one per
+      // row: an E8M0 K-block spans bytes of both wave halves.)
+      const float mrow = max_across_halves(ml);
+      if (m_ref == kNegBig && mrow != -INFINITY) m_ref = ceilf(mrow);
+      const float mi = mrow == -INFINITY ? m_ref : ceilf(mrow);
+      const float shift = 8.f - mi;
+      float psum = 0.f;
+#pragma unroll
+      for (int d = 0; d < 8; d++) {
+        const int tb = d >> 2, v = 4 * (d & 3);
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v], c_qk, shift));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 1], c_qk, shift));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 2], c_qk, shift));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 3], c_qk, shift));
+        psum += (e0 + e1) + (e2 + e3);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+        pt.pb[d] = w;
+        if constexpr (RESID) {
+          // lo = e4m3(16 (P' - hi)): hi + lo/16 holds P' to about 2^-8.
+          const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+          const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+          int wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e0 - h01[0]), 16.f * (e1 - h01[1]), 0, false);
+          wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e2 - h23[0]), 16.f * (e3 - h23[1]), wl, true);
+          pt.pbl[d] = wl;
+        } else {
+          pt.pbl[d] = 0;
+        }
+      }
+      // E8M0 biased exponent of 2^(mi - m_ref), clamped to the format
+      // (0 = 2^-127: the tile's weights are negligible there).
+      const float dexp = fminf(mi - m_ref, 64.f);
+      pt.sc = dexp < -126.f ? 0 : (int)dexp + 127;
+      pt.scl = pt.sc > 4 ? pt.sc - 4 : 0;
+      l_f += psum * __builtin_amdgcn_ldexpf(1.0f, pt.sc - 127);   // this half's exact weights
+    } else {
+      if (__builtin_amdgcn_ballot_w64(m_ref == kNegBig && ml != -INFINITY) != 0) {
+        const float mrow = max_across_halves(ml);   // first tile this row sees: agree on m_ref
+        if (m_ref == kNegBig && mrow != -INFINITY) m_ref = mrow;
+      }
+      const float shift = -m_ref;
+      float psum = 0.f;
+      // P operand: k-step kk holds the tokens of registers 8*kk .. 8*kk+7.
+      bf16x8_t pop[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[0][8 * kk + s], c_qk, shift));
+          psum += e;
+          pop[kk][s] = (__bf16)e;
+        }
+      l_f += psum;
+      const i32x4_t w0 = __builtin_bit_cast(i32x4_t, pop[0]), w1 = __builtin_bit_cast(i32x4_t, pop[1]);
+      pt.pb = i32x8_t{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      pt.pbl = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      pt.sc = pt.scl = 0;
+    }
+    return pt;
+  };
+
+  // ---- the tile loop, at most twice (second pass: exact reference)
   for (int pass = 0; pass < 2; pass++) {
 #pragma unroll
     for (int fb = 0; fb < 16; fb++) oacc[fb] = f32x16_t{};
-    l_q = 0.f;
+    lsum = f32x16_t{};
     l_f = 0.f;
-    if (pass == 1) m_ref = m_seen == -INFINITY ? kNegBig : (FP8 ? ceilf(m_seen) : m_seen);
+    if (pass == 1) {
+      const float mrow = max_across_halves(m_seen);
+      m_ref = mrow == -INFINITY ? kNegBig : (FP8 ? ceilf(mrow) : mrow);
+    }
     bool jumped = false;
 
-    // ---- prologue
+    // ---- prologue DMA
 #pragma unroll
     for (int i = 0; i < NS - 1; i++)
       if (i < n_tiles) issue_tile(i, i);
 
-    for (int i = 0; i < n_tiles; i++) {
-      wait_tiles_after<NI, NS - 2>(min(NS - 2, n_tiles - 1 - i));
-      if (RG > 1) lds_barrier();
-      if (i + NS - 1 < n_tiles) issue_tile(i + NS - 1, (i + NS - 1) % NS);
-      const LDS_AS uint8_t* tile = lds + (i % NS) * kTileBytes;
-
-      // ---- S^T = K Q^T
-      f32x16_t sacc[K::kTokBlocks];
+    if constexpr (PIPE) {
+      if (n_tiles > 0) {
+        // Tile 0: wait, QK, softmax.
+        wait_tiles_after<NI, NS - 2>(min(NS - 2, n_tiles - 1));
+        lds_barrier();
+        f32x16_t sacc[K::kTokBlocks];
+        {
+          const LDS_AS uint8_t* t0 = lds;
+          opnd_t qa[3];
+          qa[0] = ld_qk(t0, 0);
+          qa[1] = ld_qk(t0, 1);
 #pragma unroll
-      for (int tb = 0; tb < K::kTokBlocks; tb++) {
-        sacc[tb] = f32x16_t{};
-        const LDS_AS uint8_t* tb_base = tile + tb * 32 * K::kRowBytes;
-#pragma unroll
-        for (int k = 0; k < K::kQkSteps; k++) {
-          if (FP8) {
-            const i32x4_t lo = *(const LDS_AS i32x4_t*)(tb_base + a_off[0] + 64 * k);
-            const i32x4_t hi = *(const LDS_AS i32x4_t*)(tb_base + a_off[1] + 64 * k);
-            const i32x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const i32x8_t bq = {qreg[8 * k], qreg[8 * k + 1], qreg[8 * k + 2], qreg[8 * k + 3],
-                                qreg[8 * k + 4], qreg[8 * k + 5], qreg[8 * k + 6], qreg[8 * k + 7]};
-            sacc[tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bq, sacc[tb], 0, 0, 0, 127, 0, 127);
-          } else {
-            const i32x4_t a = *(const LDS_AS i32x4_t*)(tb_base + a_off[k & 3] + 128 * (k >> 2));
-            const i32x4_t bq = {qreg[4 * k], qreg[4 * k + 1], qreg[4 * k + 2], qreg[4 * k + 3]};
-            sacc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                               __builtin_bit_cast(bf16x8_t, bq), sacc[tb], 0, 0, 0);
+          for (int n = 0; n < NQK; n++) {
+            if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(t0, n + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            qk_mfma(sacc, n, qa[n % 3]);
+            __builtin_amdgcn_sched_barrier(0);
           }
+          drain_scores(sacc);
+        }
+        PTile pt = softmax(sacc, 0, jumped);
+
+        // Steady state: iteration i runs PV(i) interleaved with QK(i+1).
+        for (int i = 0; i + 1 < n_tiles; i++) {
+          // Tile i+1 must be resident; tiles up to i+NS-2 may still be in flight.
+          wait_tiles_after<NI, NS - 3>(min(NS - 3, n_tiles - 2 - i));
+          lds_barrier();   // also: every wave is done with tile i-1's slot
+          if (i + NS - 1 < n_tiles) issue_tile(i + NS - 1, (i + NS - 1) % NS);
+          const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
+          const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
+          opnd_t qa[2], va[2];
+          qa[0] = ld_qk(tq, 0);
+          va[0] = ld_pv(tv, 0);
+          // Issue order q0 v0 q1 v1 ... : each QK chain step sits three
+          // products after its predecessor; operands are read one pair ahead.
+#pragma unroll
+          for (int n = 0; n < (NQK > NPV ? NQK : NPV); n++) {
+            if (n + 1 < NQK) qa[(n + 1) & 1] = ld_qk(tq, n + 1);
+            if (n + 1 < NPV) va[(n + 1) & 1] = ld_pv(tv, n + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (n < NQK) qk_mfma(sacc, n, qa[n & 1]);
+            if (n < NPV) pv_mfma(n, va[n & 1], pt);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          row_sum_mfma(pt);
+          drain_scores(sacc);
+          pt = softmax(sacc, i + 1, jumped);
+        }
+
+        // Last tile: PV only.
+        {
+          const LDS_AS uint8_t* tv = lds + ((n_tiles - 1) % NS) * kTileBytes;
+          opnd_t va[3];
+          va[0] = ld_pv(tv, 0);
+          va[1] = ld_pv(tv, 1);
+#pragma unroll
+          for (int n = 0; n < NPV; n++) {
+            if (n + 2 < NPV) va[(n + 2) % 3] = ld_pv(tv, n + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_mfma(n, va[n % 3], pt);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          row_sum_mfma(pt);
         }
       }
-
-      // ---- masks.  Register v of token block tb holds token 32*tb + 8*(v/4) + 4*h + v%4.
-      if (SPARSE) {
-        const int phys = lane < K::kTileTok ? sp_rows[i * K::kTileTok + lane] : 0;
-        const uint64_t valid =
-            __builtin_amdgcn_ballot_w64(phys >= 0) | (K::kTileTok == 64 ? 0ull : ~0ull << 32);
-        if (valid != ~0ull) {
+    } else {
+      for (int i = 0; i < n_tiles; i++) {
+        wait_tiles_after<NI, NS - 2>(min(NS - 2, n_tiles - 1 - i));
+        if (RG > 1) lds_barrier();
+        if (i + NS - 1 < n_tiles) issue_tile(i + NS - 1, (i + NS - 1) % NS);
+        const LDS_AS uint8_t* tile = lds + (i % NS) * kTileBytes;
+        f32x16_t sacc[K::kTokBlocks];
+        {
+          opnd_t qa[3];
+          qa[0] = ld_qk(tile, 0);
+          qa[1] = ld_qk(tile, 1);
 #pragma unroll
-          for (int tb = 0; tb < K::kTokBlocks; tb++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) {
-              const int tok = 32 * tb + 8 * (v >> 2) + 4 * h + (v & 3);
-              if (!((valid >> tok) & 1)) sacc[tb][v] = -INFINITY;
-            }
-        }
-      } else {
-        const int tok0 = tok_begin + i * K::kTileTok;
-        if (tok0 + K::kTileTok > L - p.T + 1) {   // some token may lie past a row's causal limit
-#pragma unroll
-          for (int tb = 0; tb < K::kTokBlocks; tb++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) {
-              const int tok = tok0 + 32 * tb + 8 * (v >> 2) + 4 * h + (v & 3);
-              if (tok >= n_vis) sacc[tb][v] = -INFINITY;
-            }
-        }
-      }
-
-      // ---- online softmax (log2 domain)
-      float mt = -INFINITY;
-#pragma unroll
-      for (int tb = 0; tb < K::kTokBlocks; tb++)
-#pragma unroll
-        for (int v = 0; v < 16; v++) mt = fmaxf(mt, sacc[tb][v]);
-      mt = max_across_halves(mt) * c_qk;   // tile row maximum, scaled (-inf if all masked)
-      m_seen = fmaxf(m_seen, mt);
-      if (FP8) {
-        // Integer tile reference keeps every scale an exact power of two.
-        const float mi = ceilf(mt);
-        if (m_ref == kNegBig && mt != -INFINITY) m_ref = mi;
-        jumped |= mi > m_ref + 64.f;
-        // P' = 2^(x - mi + 8) in [0, 256] -> e4m3; the PV MFMA multiplies it by
-        // 2^(mi - m_ref) through the E8M0 scale of its P operand.
-        const float mref = mt == -INFINITY ? m_ref : mi;
-        const float shift = 8.f - mref;
-        // hi = e4m3(P'), lo = e4m3(16 (P' - hi)): the pair holds P' to ~2^-8.
-        float psum_f = 0.f, psum_q = 0.f, psum_lo = 0.f;
-        int pk[8], pl[8];
-#pragma unroll
-        for (int d = 0; d < 8; d++) {
-          const int tb = d >> 2, v = 4 * (d & 3);
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v], c_qk, shift));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 1], c_qk, shift));
-          const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 2], c_qk, shift));
-          const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 3], c_qk, shift));
-          psum_f += (e0 + e1) + (e2 + e3);
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
-          pk[d] = w;
-          const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-          const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-          psum_q += (h01[0] + h01[1]) + (h23[0] + h23[1]);
-          if constexpr (RESID) {
-            int wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e0 - h01[0]), 16.f * (e1 - h01[1]), 0, false);
-            wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e2 - h23[0]), 16.f * (e3 - h23[1]), wl, true);
-            pl[d] = wl;
-            const auto l01 = __builtin_amdgcn_cvt_pk_f32_fp8(wl, false);
-            const auto l23 = __builtin_amdgcn_cvt_pk_f32_fp8(wl, true);
-            psum_lo += (l01[0] + l01[1]) + (l23[0] + l23[1]);
-          } else {
-            pl[d] = 0;
+          for (int n = 0; n < NQK; n++) {
+            if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(tile, n + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            qk_mfma(sacc, n, qa[n % 3]);
+            __builtin_amdgcn_sched_barrier(0);
           }
+          drain_scores(sacc);
         }
-        psum_q = sum_across_halves(psum_q);
-        psum_f = sum_across_halves(psum_f);
-        // E8M0 biased exponent of 2^(mref - m_ref); below 2^-122 the tile is dropped.
-        const float dexp = fminf(mref - m_ref, 64.f);
-        const int sc = dexp < -122.f ? 0 : (int)dexp + 127;
-        const float pscale = sc > 0 ? __builtin_amdgcn_ldexpf(1.0f, sc - 127) : 0.f;
-        if (RESID) psum_q += sum_across_halves(psum_lo) * 0.0625f;
-        l_q += psum_q * pscale;
-        l_f += psum_f * pscale;
-        const i32x8_t pz = {0, 0, 0, 0, 0, 0, 0, 0};
-        const i32x8_t pop = {pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
-        const i32x8_t pb = sc > 0 ? pop : pz;
-        const int scl = sc > 4 ? sc - 4 : 0;
-        const i32x8_t plo = {pl[0], pl[1], pl[2], pl[3], pl[4], pl[5], pl[6], pl[7]};
-        const i32x8_t pbl = sc > 4 ? plo : pz;
-        // ---- O^T += V^T P^T  (+ V^T Plo^T 2^-4)
+        const PTile pt = softmax(sacc, i, jumped);
+        opnd_t va[3];
+        va[0] = ld_pv(tile, 0);
+        va[1] = ld_pv(tile, 1);
 #pragma unroll
-        for (int fb = 0; fb < 16; fb++) {
-          i32x8_t a;
-#pragma unroll
-          for (int r = 0; r < 4; r++) {
-            const i32x2_t d =
-                __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2_t*)(tile + v_off[r][fb & 1] + 32 * fb));
-            a[2 * r] = d[0];
-            a[2 * r + 1] = d[1];
-          }
-          oacc[fb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[fb], 0, 0, 0, 127, 0, sc);
-          if constexpr (RESID)
-            oacc[fb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pbl, oacc[fb], 0, 0, 0, 127, 0, scl);
+        for (int n = 0; n < NPV; n++) {
+          if (n + 2 < NPV) va[(n + 2) % 3] = ld_pv(tile, n + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          pv_mfma(n, va[n % 3], pt);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      } else {
-        if (m_ref == kNegBig && mt != -INFINITY) m_ref = mt;
-        jumped |= mt > m_ref + 64.f;
-        const float shift = -m_ref;
-        float psum_f = 0.f, psum_q = 0.f;
-        // P operand: k-step kk holds the tokens of registers 8*kk .. 8*kk+7.
-        bf16x8_t pop[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-          for (int s = 0; s < 8; s++) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[0][8 * kk + s], c_qk, shift));
-            const __bf16 eb = (__bf16)e;
-            psum_f += e;
-            psum_q += (float)eb;      // the rounded weight the PV product uses
-            pop[kk][s] = eb;
-          }
-        l_q += sum_across_halves(psum_q);
-        l_f += sum_across_halves(psum_f);
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int fb = 0; fb < 16; fb++) {
-#pragma unroll
-          for (int kk = 0; kk < 2; kk++) {
-            const i16x4_t d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (LDS_AS i16x4_t*)(tile + v_off[0][fb & 1] + 64 * fb + 16 * kk * K::kRowBytes));
-            const i16x4_t d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (LDS_AS i16x4_t*)(tile + v_off[1][fb & 1] + 64 * fb + 16 * kk * K::kRowBytes));
-            typedef short i16x8_t __attribute__((ext_vector_type(8)));
-            const i16x8_t cat = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-            oacc[fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cat), pop[kk],
-                                                               oacc[fb], 0, 0, 0);
-          }
-        }
+        row_sum_mfma(pt);
       }
     }
+    mfma_drain(lsum);
 
     // ---- second pass needed?  (workgroup-uniform: all waves share the DMA)
     if (pass == 1) break;
@@ -562,6 +742,8 @@ mla_partial_kernel(const PartialParams p) {
 
   // ---- epilogue: normalize, write final output or the split partial
   const float off = FP8 ? 8.f : 0.f;
+  l_f = sum_across_halves(l_f);
+  const float l_q = lsum[0];       // every element of a lane's lsum holds its row's sum
   const bool empty = !(l_f > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_q;
   const float lse_v = empty ? -INFINITY : (m_ref - off + __builtin_amdgcn_logf(l_f)) * kLn2;

@@ -76,6 +76,21 @@ def test_heuristic_fills_the_chip(lib):
     assert binding.num_kv_splits(1, 1, 16, 10000, 5000, False) >= 3
 
 
+def test_launch_waves_follow_the_row_block_rules(lib):
+    # 128 rows and enough units to fill the chip: one four-wave row block.
+    assert binding.launch_waves(64, 4, 32, 80000, 0, True) == 4
+    assert binding.launch_waves(32, 8, 128, 32768, 0, False) == 4
+    assert binding.launch_waves(256, 1, 128, 300, 0, False) == 4
+    # 16 rows per sequence fit one wave.
+    assert binding.launch_waves(128, 1, 16, 8192, 0, False) == 1
+    # Few short units: narrower row blocks fill the chip instead of splits.
+    assert binding.launch_waves(2, 1, 128, 300, 0, False) == 1
+    assert binding.launch_waves(4, 1, 64, 300, 0, False) == 1
+    # 64 rows and units enough for two workgroups per compute unit: two waves.
+    assert binding.launch_waves(512, 1, 64, 300, 0, False) == 2
+    assert binding.launch_waves(1, 0, 16, 100) == 0
+
+
 def test_invalid_sizes_are_rejected(lib):
     assert binding.num_kv_splits(1, 0, 16, 100) == 0
     assert binding.num_kv_splits(1, 9, 16, 100) == 0

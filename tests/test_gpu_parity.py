@@ -223,6 +223,72 @@ def test_sparse_all_positions_equals_dense():
     assert torch.max(torch.abs(l_s - l_d)).item() < 1e-5
 
 
+# ------------------------------------------------------------------ four-wave (pipelined) variants
+
+# Shapes whose launch plan puts four waves (128 query rows) in a workgroup:
+# the software-pipelined tile loop.  Few work units make the planner narrow
+# the row block instead, so these batches are wide.
+FOUR_WAVE = [
+    ("bf16", 256, 128, 1, (32, 330), 0),
+    ("bf16", 256, 32, 4, (3, 700), 0),
+    ("bf16", 32, 128, 8, (60, 900), 0),
+    ("fp8", 256, 32, 4, (3, 700), 0),
+    ("fp8", 256, 128, 1, (32, 330), 0),
+    ("sparse", 256, 128, 1, (100, 900), 96),
+]
+
+
+@pytest.mark.parametrize("kind,B,H,T,lens,K", FOUR_WAVE)
+def test_four_wave_variants(kind, B, H, T, lens, K):
+    kv_dtype = "fp8" if kind == "fp8" else "bf16"
+    inp = wl.make_inputs(B, H, T, lens, kv_dtype=kv_dtype, out_dtype="f32", topk=K or None, seed=31 + B + H + T,
+                         poison=True)
+    assert binding.launch_waves(B, T, H, inp.max_len, K, kv_dtype == "fp8") == 4
+    out, lse = run_case(inp, 0, "four-wave %s" % kind)
+    rows = sample_rows(B * T * H, 160, seed=B + H)
+    ref_o, ref_l = oracle_rows(inp, rows=rows)
+    compare(out, lse, ref_o, ref_l, kv_dtype, rows=rows, what="four-wave %s" % kind)
+
+
+# ------------------------------------------------------------------ second pass (large logit jump)
+
+def _plant_large_logit(inp, pos):
+    """Cache position `pos` of every sequence becomes a key aligned with the
+    query of that sequence's row (t=0, h=0), so that row's logit there lies
+    far above its first tile's (more than 2^64 in the log2 domain): the
+    kernel must rerun the unit against the exact row maximum."""
+    for b in range(inp.B):
+        pg = int(inp.block_table[b, pos // 64])
+        if inp.kv_dtype == "bf16":
+            q = torch.cat([inp.q_nope[b, 0, 0], inp.q_pe[b, 0, 0]]).float()
+            inp.kv_cache[pg, pos % 64] = (3.0 * q).to(torch.bfloat16)
+        else:
+            q = torch.cat([inp.q_nope[b, 0, 0], inp.q_pe[b, 0, 0]]).view(torch.float8_e4m3fn).float()
+            inp.kv_cache[pg, pos % 64] = torch.where(q >= 0, 448.0, -448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return inp
+
+
+@pytest.mark.parametrize("kind,B,H,T,waves", [
+    ("bf16", 256, 32, 4, 4), ("bf16", 256, 128, 1, 4), ("bf16", 4, 16, 1, 1), ("bf16", 512, 64, 1, 2),
+    ("fp8", 256, 32, 4, 4), ("fp8", 4, 16, 1, 1),
+    ("sparse", 256, 128, 1, 4), ("sparse", 4, 16, 1, 1),
+])
+def test_large_logit_jump_reruns_against_exact_maximum(kind, B, H, T, waves):
+    L, pos = 300, 150
+    kv_dtype = "fp8" if kind == "fp8" else "bf16"
+    K = 96 if kind == "sparse" else 0
+    inp = wl.make_inputs(B, H, T, [L] * B, kv_dtype=kv_dtype, out_dtype="f32", topk=K or None, seed=41 + B + H)
+    if K:
+        inp.topk_indices[:, :, K // 2] = pos    # the planted position sits in the second index tile
+    _plant_large_logit(inp, pos)
+    assert binding.launch_waves(B, T, H, L, K, kv_dtype == "fp8") == waves
+    out, lse = run_case(inp, 0, "logit jump %s" % kind)
+    rows = np.unique(np.concatenate([sample_rows(B * T * H, 96, seed=B), np.arange(0, B * T * H, T * H)[:16]]))
+    ref_o, ref_l = oracle_rows(inp, rows=rows)
+    assert np.max(ref_l) > 80.0                 # the planted logit dominates row (b, 0, 0)
+    compare(out, lse, ref_o, ref_l, kv_dtype, rows=rows, what="logit jump %s" % kind)
+
+
 # ------------------------------------------------------------------ graph capture
 
 def test_hip_graph_replay_matches_eager():
