@@ -143,6 +143,23 @@ __device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_byte_addr) : "memory");
 }
 
+// 16-byte buffer -> LDS DMA: lane i reads rsrc.base + voff_i + soff and
+// writes LDS bytes [m0 + 16 i, m0 + 16 i + 16).  An offset at or past the
+// descriptor's size reads zeros (no memory access), which is how missing
+// tokens of a tile become zero vectors.  Inline asm for the same reason as
+// dma16().
+__device__ inline void dma16_buf(int voff, i32x4_t rsrc, int soff, uint32_t lds_byte_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_byte_addr)
+               : "memory");
+}
+// Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, size in bytes.
+__device__ inline i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
 // MFMAs whose accumulator must stay in VGPRs.  The output accumulator O
 // fills all 256 AGPRs; the compiler would otherwise give the score and
 // row-sum accumulators AGPRs too and shuttle two O tiles through VGPRs on
@@ -318,52 +335,64 @@ mla_partial_kernel(const PartialParams p) {
   // ---- DMA source offsets.  Wave w fills tile units [w*NI*64, (w+1)*NI*64):
   // instruction j writes LDS units pos = (w*NI + j)*64 + lane, i.e. token
   // t = pos / kUnits, swizzled unit c' = pos % kUnits, and so fetches global
-  // unit (t, c' ^ swz(t)).
-  int dma_off[NPRE];   // byte offset inside the tile's global rows
+  // unit (t, c' ^ swz(t)).  The pattern repeats every NPRE instructions (16
+  // tokens) when NI > 18.  Kept per lane as token | (byte in token) << 8.
+  int dma_tc[NPRE];
 #pragma unroll
   for (int j = 0; j < NPRE; j++) {
     const int pos = (wave * NI + j) * 64 + lane;
     const int t = pos / K::kUnits;
     const int c = (pos % K::kUnits) ^ K::swz(t);
-    dma_off[j] = t * K::kRowBytes + 16 * c;
+    dma_tc[j] = SPARSE ? (t | (16 * c) << 8) : t * K::kRowBytes + 16 * c;   // dense: byte offset in the tile
   }
-  // Period: NPRE instructions cover exactly 16 tokens when NI > 18.
-  constexpr int kPeriodBytes = 16 * K::kRowBytes;
+  const uint32_t lds_u32 = (uint32_t)(uintptr_t)lds;
 
-  auto issue_tile = [&](int i, int slot) {
-    const uint32_t dst = (uint32_t)(uintptr_t)(lds + slot * kTileBytes + wave * NI * 1024);
+  // Source of one tile's DMA.  Dense: a buffer descriptor over the tile's
+  // existing tokens (past the sequence, a bad page or a tile past the end
+  // of the unit: fewer or no bytes, so those reads return zeros).  Sparse:
+  // the tile's slice of the row table (n_valid = 0 for a tile past the end).
+  struct DmaSrc {
+    i32x4_t rsrc;
+    LDS_AS const int* rows;
+    int n_valid;
+  };
+  auto dma_prepare = [&](int i) -> DmaSrc {
+    DmaSrc d;
+    const bool real = i < n_tiles;
     if (SPARSE) {
-      LDS_AS const int* rows_tab = table + i * K::kTileTok;
-#pragma unroll
-      for (int j = 0; j < NI; j++) {
-        const int off = dma_off[j % NPRE] + (j / NPRE) * kPeriodBytes;
-        const int t = off / K::kRowBytes;
-        const int cb = off - t * K::kRowBytes;
-        const int phys = rows_tab[t];
-        const uint8_t* src = phys >= 0 ? p.kv + (int64_t)phys * K::kRowBytes + cb : g_zero_row + cb;
-        dma16(src, dst + j * 1024);
-      }
+      d.rsrc = i32x4_t{0, 0, 0, 0};
+      d.rows = table + (real ? i : 0) * K::kTileTok;
+      d.n_valid = real ? K::kTileTok : 0;
     } else {
-      const int tok0 = tok_begin + i * K::kTileTok;     // first token of the tile
-      const int pg = table[(tok0 >> 6) - page0];        // same address in every lane: LDS broadcast
-      const uint8_t* base = p.kv + ((int64_t)(pg >= 0 ? pg : 0) * 64 + (tok0 & 63)) * K::kRowBytes;
-      const int n_valid = pg >= 0 ? min(K::kTileTok, L - tok0) : 0;
-      if (n_valid == K::kTileTok) {
-#pragma unroll
-        for (int j = 0; j < NI; j++) {
-          const int off = dma_off[j % NPRE] + (j / NPRE) * kPeriodBytes;
-          dma16(base + off, dst + j * 1024);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NI; j++) {
-          const int off = dma_off[j % NPRE] + (j / NPRE) * kPeriodBytes;
-          const int t = off / K::kRowBytes;
-          const uint8_t* src = t < n_valid ? base + off : g_zero_row + (off - t * K::kRowBytes);
-          dma16(src, dst + j * 1024);
-        }
-      }
+      const int tok0 = tok_begin + (real ? i : 0) * K::kTileTok;
+      const int pg = n_tiles > 0 ? table[(tok0 >> 6) - page0] : -1;   // same address in every lane
+      const int n_valid = (real && pg >= 0) ? min(K::kTileTok, L - tok0) : 0;
+      d.rsrc = buffer_rsrc(p.kv + ((int64_t)(pg >= 0 ? pg : 0) * 64 + (tok0 & 63)) * K::kRowBytes,
+                           (uint32_t)(n_valid * K::kRowBytes));
+      d.rows = table;
+      d.n_valid = n_valid;
     }
+    return d;
+  };
+  // DMA instruction j of a tile into ring slot `slot`.
+  auto dma_issue = [&](const DmaSrc& d, int slot, int j) {
+    const uint32_t dst = lds_u32 + slot * kTileBytes + (wave * NI + j) * 1024;
+    if (SPARSE) {
+      const int tc = dma_tc[j % NPRE];
+      const int t = (tc & 255) + (j / NPRE) * 16;
+      const int cb = tc >> 8;
+      const int phys = d.rows[t];
+      const uint8_t* src =
+          (t < d.n_valid && phys >= 0) ? p.kv + (int64_t)phys * K::kRowBytes + cb : g_zero_row;
+      dma16(src, dst);
+    } else {
+      dma16_buf(dma_tc[j % NPRE], d.rsrc, (j / NPRE) * 16 * K::kRowBytes, dst);
+    }
+  };
+  auto issue_tile = [&](int i, int slot) {
+    const DmaSrc d = dma_prepare(i);
+#pragma unroll
+    for (int j = 0; j < NI; j++) dma_issue(d, slot, j);
   };
 
   // ---- per-lane LDS read offsets (within a tile)
@@ -512,23 +541,32 @@ mla_partial_kernel(const PartialParams p) {
     else mfma_drain(sacc[0]);
   };
 
-  // Mask + softmax of tile i from its scores; updates the row state.
-  auto softmax = [&](f32x16_t (&sacc)[K::kTokBlocks], int i, bool& jumped) -> PTile {
-    // Register v of token block tb holds token 32*tb + 8*(v/4) + 4*h + v%4.
-    // The masks compare that compile-time offset (without the 4*h) against
-    // one per-lane quantity, so no per-register index lives in a VGPR.
+  // ---- softmax of one tile, in stages.  The pipelined loop places the
+  // stages between the PV products of the previous tile, so that their
+  // VALU work runs while the matrix core is busy.
+  //
+  // Register v of token block tb holds token 32*tb + 8*(v/4) + 4*h + v%4.
+  constexpr int NEXP = FP8 ? 8 : 4;      // exponent stages, four scores each
+  struct SmState {
+    float ml;       // this lane's running maximum of the tile's scores
+    float shift;    // exponent offset applied to scaled scores
+    float psum;     // this lane's sum of the unrounded weights
+  };
+
+  // Mask: compare each register's compile-time token offset (without the
+  // 4*h) against one per-lane limit.  Selects, not branches: a branch here
+  // splits the loop body and costs far more registers.
+  auto sm_mask = [&](f32x16_t (&sacc)[K::kTokBlocks], int i) {
     if (SPARSE) {
       const int phys = lane < K::kTileTok ? table[i * K::kTileTok + lane] : 0;
       const uint64_t valid = __builtin_amdgcn_ballot_w64(phys >= 0) | (K::kTileTok == 64 ? 0ull : ~0ull << 32);
-      const uint64_t mine = valid >> (4 * h);   // branch-free, as below
+      const uint64_t mine = valid >> (4 * h);
 #pragma unroll
       for (int tb = 0; tb < K::kTokBlocks; tb++)
 #pragma unroll
         for (int v = 0; v < 16; v++)
           sacc[tb][v] = (mine >> (32 * tb + 8 * (v >> 2) + (v & 3))) & 1 ? sacc[tb][v] : -INFINITY;
     } else {
-      // Branch-free: a branch here splits the pipelined loop body and costs
-      // far more registers than these selects.
       const int lim = n_vis - (tok_begin + i * K::kTileTok) - 4 * h;   // offsets at or past lim are masked
 #pragma unroll
       for (int tb = 0; tb < K::kTokBlocks; tb++)
@@ -536,78 +574,185 @@ mla_partial_kernel(const PartialParams p) {
         for (int v = 0; v < 16; v++)
           sacc[tb][v] = 32 * tb + 8 * (v >> 2) + (v & 3) < lim ? sacc[tb][v] : -INFINITY;
     }
-    float ml = -INFINITY;
+  };
+  // Stage "max of token block tb".
+  auto sm_max_block = [&](f32x16_t (&sacc)[K::kTokBlocks], int tb, SmState& st) {
+    float m = tb == 0 ? -INFINITY : st.ml;
 #pragma unroll
-    for (int tb = 0; tb < K::kTokBlocks; tb++)
-#pragma unroll
-      for (int v = 0; v < 16; v++) ml = fmaxf(ml, sacc[tb][v]);
-    ml *= c_qk;                          // this lane's maximum, scaled (-inf if all masked)
+    for (int v = 0; v < 16; v++) m = fmaxf(m, sacc[tb][v]);
+    st.ml = m;
+  };
+  // Stage "row maximum": reference, per-tile shift and (fp8) P scales.
+  auto sm_max_row = [&](bool& jumped, SmState& st, PTile& pt) {
+    const float ml = st.ml * c_qk;       // this lane's maximum, scaled (-inf if all masked)
     m_seen = fmaxf(m_seen, ml);
     // A jump is measured against a reference already set by an earlier tile.
     jumped |= m_ref != kNegBig && ml > m_ref + 64.f;
-    PTile pt;
+    const float mrow = max_across_halves(ml);
     if constexpr (FP8) {
       // P' = 2^(x - mi + 8) in [0, 256] -> e4m3, with mi the integer ceiling
       // of the row's tile maximum; the PV MFMA multiplies it by 2^(mi - m_ref)
       // through the E8M0 scale of its P operand.  (The scale must be one per
       // row: an E8M0 K-block spans bytes of both wave halves.)
-      const float mrow = max_across_halves(ml);
       if (m_ref == kNegBig && mrow != -INFINITY) m_ref = ceilf(mrow);
       const float mi = mrow == -INFINITY ? m_ref : ceilf(mrow);
-      const float shift = 8.f - mi;
-      float psum = 0.f;
-#pragma unroll
-      for (int d = 0; d < 8; d++) {
-        const int tb = d >> 2, v = 4 * (d & 3);
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v], c_qk, shift));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 1], c_qk, shift));
-        const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 2], c_qk, shift));
-        const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 3], c_qk, shift));
-        psum += (e0 + e1) + (e2 + e3);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
-        pt.pb[d] = w;
-        if constexpr (RESID) {
-          // lo = e4m3(16 (P' - hi)): hi + lo/16 holds P' to about 2^-8.
-          const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-          const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-          int wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e0 - h01[0]), 16.f * (e1 - h01[1]), 0, false);
-          wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e2 - h23[0]), 16.f * (e3 - h23[1]), wl, true);
-          pt.pbl[d] = wl;
-        } else {
-          pt.pbl[d] = 0;
-        }
-      }
+      st.shift = 8.f - mi;
       // E8M0 biased exponent of 2^(mi - m_ref), clamped to the format
       // (0 = 2^-127: the tile's weights are negligible there).
       const float dexp = fminf(mi - m_ref, 64.f);
       pt.sc = dexp < -126.f ? 0 : (int)dexp + 127;
       pt.scl = pt.sc > 4 ? pt.sc - 4 : 0;
-      l_f += psum * __builtin_amdgcn_ldexpf(1.0f, pt.sc - 127);   // this half's exact weights
     } else {
-      if (__builtin_amdgcn_ballot_w64(m_ref == kNegBig && ml != -INFINITY) != 0) {
-        const float mrow = max_across_halves(ml);   // first tile this row sees: agree on m_ref
-        if (m_ref == kNegBig && mrow != -INFINITY) m_ref = mrow;
-      }
-      const float shift = -m_ref;
-      float psum = 0.f;
-      // P operand: k-step kk holds the tokens of registers 8*kk .. 8*kk+7.
-      bf16x8_t pop[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-        for (int s = 0; s < 8; s++) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[0][8 * kk + s], c_qk, shift));
-          psum += e;
-          pop[kk][s] = (__bf16)e;
-        }
-      l_f += psum;
-      const i32x4_t w0 = __builtin_bit_cast(i32x4_t, pop[0]), w1 = __builtin_bit_cast(i32x4_t, pop[1]);
-      pt.pb = i32x8_t{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-      pt.pbl = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      if (m_ref == kNegBig && mrow != -INFINITY) m_ref = mrow;
+      st.shift = -m_ref;
       pt.sc = pt.scl = 0;
     }
-    return pt;
+    st.psum = 0.f;
+  };
+  // Stage "exponents of registers 4d .. 4d+3" (fp8: token block d/4).
+  auto sm_exp = [&](f32x16_t (&sacc)[K::kTokBlocks], int d, SmState& st, PTile& pt) {
+    const int tb = FP8 ? d >> 2 : 0;
+    const int v = FP8 ? 4 * (d & 3) : 4 * d;
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v], c_qk, st.shift));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 1], c_qk, st.shift));
+    const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 2], c_qk, st.shift));
+    const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 3], c_qk, st.shift));
+    st.psum += (e0 + e1) + (e2 + e3);
+    if constexpr (FP8) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+      pt.pb[d] = w;
+      if constexpr (RESID) {
+        // lo = e4m3(16 (P' - hi)): hi + lo/16 holds P' to about 2^-8.
+        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        int wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e0 - h01[0]), 16.f * (e1 - h01[1]), 0, false);
+        wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e2 - h23[0]), 16.f * (e3 - h23[1]), wl, true);
+        pt.pbl[d] = wl;
+      } else {
+        pt.pbl[d] = 0;
+      }
+    } else {
+      // P operand: registers 8*kk .. 8*kk+7 form k-step kk; two bf16 per dword.
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t lo = {(__bf16)e0, (__bf16)e1};
+      const bf16x2_t hi = {(__bf16)e2, (__bf16)e3};
+      pt.pb[2 * d] = __builtin_bit_cast(int, lo);
+      pt.pb[2 * d + 1] = __builtin_bit_cast(int, hi);
+    }
+  };
+  // Stage "finish": this half's unrounded weights join l_f.
+  auto sm_finish = [&](const SmState& st, const PTile& pt) {
+    if constexpr (FP8) l_f += st.psum * __builtin_amdgcn_ldexpf(1.0f, pt.sc - 127);
+    else l_f += st.psum;
+  };
+  // Stage k of a tile's softmax (compile-time k once loops are unrolled);
+  // returns false past the last stage.
+  constexpr int NSTAGE_CLEAN = K::kTokBlocks + 1 + NEXP + 1;
+  auto sm_stage = [&](int k, bool mask, f32x16_t (&sacc)[K::kTokBlocks], int i, bool& jumped, SmState& st,
+                      PTile& pt) {
+    if (mask) {
+      if (k == 0) { sm_mask(sacc, i); return; }
+      k -= 1;
+    }
+    if (k < K::kTokBlocks) sm_max_block(sacc, k, st);
+    else if (k == K::kTokBlocks) sm_max_row(jumped, st, pt);
+    else if (k < K::kTokBlocks + 1 + NEXP) sm_exp(sacc, k - K::kTokBlocks - 1, st, pt);
+    else if (k == K::kTokBlocks + 1 + NEXP) sm_finish(st, pt);
+  };
+  auto softmax_all = [&](f32x16_t (&sacc)[K::kTokBlocks], int i, bool& jumped, PTile& pt) {
+    SmState st;
+#pragma unroll
+    for (int k = 0; k < NSTAGE_CLEAN + 1; k++) sm_stage(k, true, sacc, i, jumped, st, pt);
+  };
+
+  // ---- tiles [0, n_clean) need no mask: every row sees all their tokens
+  // (dense: the tile ends at or before the first draft row's causal limit).
+  // The tiles after them take the masked softmax.
+  int n_clean = 0;
+  if (!SPARSE) {
+    const int lim0 = L - p.T + 1 - tok_begin;
+    n_clean = lim0 > 0 ? min(n_tiles, lim0 / K::kTileTok) : 0;
+  }
+
+  // ---- one step of the pipelined loop (four waves): QK of tile i+1 with
+  // the DMA of tile i+NS-1 spread between its products, then the softmax
+  // of tile i+1 in stages between the PV products of tile i.
+  auto pipe_step = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped,
+                       auto mask_c) __attribute__((always_inline)) {
+    constexpr bool mask = decltype(mask_c)::value;
+    // Tile i+1 resident (one tile may still be in flight behind it); every
+    // wave is done with tile i-1, whose slot the DMA below refills.
+    wait_vmcnt<NI * (NS - 3)>();
+    lds_barrier();
+    const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
+    const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
+    const int nxt = i + NS - 1;                  // past the end: a zero fill of a free slot
+    const DmaSrc src = dma_prepare(nxt);
+    constexpr int DSTRIDE = NQK / NI;
+    static_assert(NQK % NI == 0, "DMA spread");
+    opnd_t qa[3], va[3];
+    qa[0] = ld_qk(tq, 0);
+    qa[1] = ld_qk(tq, 1);
+#pragma unroll
+    for (int n = 0; n < NQK; n++) {
+      if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(tq, n + 2);
+      if (n == NQK - 2) va[0] = ld_pv(tv, 0);
+      if (n == NQK - 1) va[1] = ld_pv(tv, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      qk_mfma(sacc, n, qa[n % 3]);
+      if (n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    drain_scores(sacc);
+    PTile pn;
+    SmState st;
+#pragma unroll
+    for (int n = 0; n < NPV; n++) {
+      if (n + 2 < NPV) va[(n + 2) % 3] = ld_pv(tv, n + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_mfma(n, va[n % 3], pt);
+      sm_stage(n, mask, sacc, i + 1, jumped, st, pn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    static_assert(NSTAGE_CLEAN + 1 <= NPV, "softmax stages fit between the PV products");
+    row_sum_mfma(pt);
+    pt = pn;
+  };
+
+  // bf16 form of the step: its query operand takes 144 VGPRs, which leaves
+  // no room to keep scores live across the PV products.  QK of tile i+1 and
+  // PV of tile i alternate product by product instead, and the (short)
+  // softmax follows them.
+  auto pipe_step_qv = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped,
+                          auto mask_c) __attribute__((always_inline)) {
+    constexpr bool mask = decltype(mask_c)::value;
+    wait_vmcnt<NI * (NS - 3)>();
+    lds_barrier();
+    const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
+    const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
+    const int nxt = i + NS - 1;
+    const DmaSrc src = dma_prepare(nxt);
+    constexpr int DSTRIDE = NQK / NI;
+    static_assert(NQK % NI == 0, "DMA spread");
+    opnd_t qa[2], va[2];
+    qa[0] = ld_qk(tq, 0);
+    va[0] = ld_pv(tv, 0);
+#pragma unroll
+    for (int n = 0; n < (NQK > NPV ? NQK : NPV); n++) {
+      if (n + 1 < NQK) qa[(n + 1) & 1] = ld_qk(tq, n + 1);
+      if (n + 1 < NPV) va[(n + 1) & 1] = ld_pv(tv, n + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (n < NQK) qk_mfma(sacc, n, qa[n & 1]);
+      if (n < NPV) pv_mfma(n, va[n & 1], pt);
+      if (n < NQK && n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    row_sum_mfma(pt);
+    drain_scores(sacc);
+    SmState st;
+#pragma unroll
+    for (int k = 0; k < NSTAGE_CLEAN + 1; k++) sm_stage(k, mask, sacc, i + 1, jumped, st, pt);
   };
 
   // ---- the tile loop, at most twice (second pass: exact reference)
@@ -622,58 +767,38 @@ mla_partial_kernel(const PartialParams p) {
     }
     bool jumped = false;
 
-    // ---- prologue DMA
-#pragma unroll
-    for (int i = 0; i < NS - 1; i++)
-      if (i < n_tiles) issue_tile(i, i);
-
     if constexpr (PIPE) {
       if (n_tiles > 0) {
-        // Tile 0: wait, QK, softmax.
-        wait_tiles_after<NI, NS - 2>(min(NS - 2, n_tiles - 1));
+        // Prologue: NS-1 tiles in flight (zero fills past the end keep the
+        // count uniform), then QK and softmax of tile 0.
+#pragma unroll
+        for (int i = 0; i < NS - 1; i++) issue_tile(i, i);
+        wait_vmcnt<NI * (NS - 2)>();
         lds_barrier();
         f32x16_t sacc[K::kTokBlocks];
         {
-          const LDS_AS uint8_t* t0 = lds;
           opnd_t qa[3];
-          qa[0] = ld_qk(t0, 0);
-          qa[1] = ld_qk(t0, 1);
+          qa[0] = ld_qk(lds, 0);
+          qa[1] = ld_qk(lds, 1);
 #pragma unroll
           for (int n = 0; n < NQK; n++) {
-            if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(t0, n + 2);
+            if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(lds, n + 2);
             __builtin_amdgcn_sched_barrier(0);
             qk_mfma(sacc, n, qa[n % 3]);
             __builtin_amdgcn_sched_barrier(0);
           }
           drain_scores(sacc);
         }
-        PTile pt = softmax(sacc, 0, jumped);
+        PTile pt;
+        softmax_all(sacc, 0, jumped, pt);
 
-        // Steady state: iteration i runs PV(i) interleaved with QK(i+1).
-        for (int i = 0; i + 1 < n_tiles; i++) {
-          // Tile i+1 must be resident; tiles up to i+NS-2 may still be in flight.
-          wait_tiles_after<NI, NS - 3>(min(NS - 3, n_tiles - 2 - i));
-          lds_barrier();   // also: every wave is done with tile i-1's slot
-          if (i + NS - 1 < n_tiles) issue_tile(i + NS - 1, (i + NS - 1) % NS);
-          const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
-          const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
-          opnd_t qa[2], va[2];
-          qa[0] = ld_qk(tq, 0);
-          va[0] = ld_pv(tv, 0);
-          // Issue order q0 v0 q1 v1 ... : each QK chain step sits three
-          // products after its predecessor; operands are read one pair ahead.
-#pragma unroll
-          for (int n = 0; n < (NQK > NPV ? NQK : NPV); n++) {
-            if (n + 1 < NQK) qa[(n + 1) & 1] = ld_qk(tq, n + 1);
-            if (n + 1 < NPV) va[(n + 1) & 1] = ld_pv(tv, n + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            if (n < NQK) qk_mfma(sacc, n, qa[n & 1]);
-            if (n < NPV) pv_mfma(n, va[n & 1], pt);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          row_sum_mfma(pt);
-          drain_scores(sacc);
-          pt = softmax(sacc, i + 1, jumped);
+        int i = 0;
+        if constexpr (FP8) {
+          for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, std::false_type{});
+          for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, std::true_type{});
+        } else {
+          for (; i + 1 < n_clean; i++) pipe_step_qv(i, sacc, pt, jumped, std::false_type{});
+          for (; i + 1 < n_tiles; i++) pipe_step_qv(i, sacc, pt, jumped, std::true_type{});
         }
 
         // Last tile: PV only.
@@ -691,8 +816,12 @@ mla_partial_kernel(const PartialParams p) {
           }
           row_sum_mfma(pt);
         }
+        wait_vmcnt<0>();   // the zero fills past the end must land before the LDS is reused
       }
     } else {
+#pragma unroll
+      for (int i = 0; i < NS - 1; i++)
+        if (i < n_tiles) issue_tile(i, i);
       for (int i = 0; i < n_tiles; i++) {
         wait_tiles_after<NI, NS - 2>(min(NS - 2, n_tiles - 1 - i));
         if (RG > 1) lds_barrier();
@@ -712,7 +841,8 @@ mla_partial_kernel(const PartialParams p) {
           }
           drain_scores(sacc);
         }
-        const PTile pt = softmax(sacc, i, jumped);
+        PTile pt;
+        softmax_all(sacc, i, jumped, pt);
         opnd_t va[3];
         va[0] = ld_pv(tile, 0);
         va[1] = ld_pv(tile, 1);
