@@ -11,7 +11,7 @@ constexpr int kTokenDim = 576;
 constexpr int kPage = 64;
 constexpr int kPartialWidth = kLatentDim + 1;   // normalized outputs, then the chunk's lse
 constexpr int kSparseChunkMax = 2048;           // top-k entries one workgroup handles
-constexpr int kDensePagesMax = 2048;            // pages one workgroup handles (131072 tokens)
+constexpr int kDensePagesMax = 1024;            // pages one workgroup handles (65536 tokens)
 constexpr int kNumCUs = 256;                    // MI355X compute units
 
 struct PartialParams {

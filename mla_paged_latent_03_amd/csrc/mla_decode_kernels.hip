@@ -110,6 +110,13 @@ __device__ inline void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS accesses have completed.
+__device__ inline void wait_lgkm0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+  asm volatile("" ::: "memory");
+}
+
 template <int NI, int MAXR>
 __device__ inline void wait_tiles_after(int remaining) {
   // Wait until at most `remaining` tiles (NI loads each) are still in flight.
@@ -205,7 +212,7 @@ __device__ inline void mfma_drain(f32x16_t& a, f32x16_t& b) {
 // With four waves (RG = 4) the tile loop is software-pipelined: the QK
 // products of tile i+1 are issued interleaved with the PV products of tile
 // i, so the two dependent QK accumulator chains never stall the matrix pipe.
-template <bool FP8, bool SPARSE, int RG, int NS, bool RESID>
+template <bool FP8, bool SPARSE, int RG, int NS, bool RESID, bool FS>
 __global__ void __launch_bounds__(64 * RG) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_partial_kernel(const PartialParams p) {
   using K = Kv<FP8>;
@@ -214,13 +221,18 @@ mla_partial_kernel(const PartialParams p) {
   static_assert(NI % NPRE == 0, "DMA offset period");
   constexpr bool PIPE = RG == 4;
   static_assert(!PIPE || NS >= 3, "the pipelined loop keeps two tiles resident");
+  static_assert(!FS || (FP8 && !SPARSE && RG == 4 && !RESID), "feature split: dense fp8, four waves");
   constexpr int kTableCap = SPARSE ? kSparseChunkMax : kDensePagesMax;
+  constexpr int kPBytes = FS ? 4 * 2048 : 0;      // FS: P tile of each row block (64 lanes x 32 B)
+  constexpr int kScBytes = FS ? 4 * 32 * 4 : 0;   // FS: E8M0 scale of each row of the block
 
-  // LDS: [ring of NS tiles][unit table: int32 x kTableCap][redo flag]
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kTileBytes + kTableCap * 4 + 16];
+  // LDS: [ring of NS tiles][unit table: int32 x kTableCap][FS: P tiles][FS: scales][redo flag]
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kTileBytes + kTableCap * 4 + kPBytes + kScBytes + 16];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
   LDS_AS int* table = (LDS_AS int*)(lds + NS * kTileBytes);
-  LDS_AS int* redo_flag = table + kTableCap;
+  LDS_AS uint8_t* pbuf = lds + NS * kTileBytes + kTableCap * 4;
+  LDS_AS int* scbuf = (LDS_AS int*)(pbuf + kPBytes);
+  LDS_AS int* redo_flag = (LDS_AS int*)(pbuf + kPBytes + kScBytes);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -720,6 +732,98 @@ mla_partial_kernel(const PartialParams p) {
     pt = pn;
   };
 
+  // ---- feature split (FS): wave w accumulates O for all four row blocks
+  // of the workgroup over output features [128 w, 128 w + 128), so every
+  // byte of V is read from LDS by one wave instead of four.  The P tile
+  // (fp8, in the B-operand layout) and the E8M0 scales of each row block
+  // pass from the wave that computed them to the others through LDS.
+  // oacc[4 * rq + fs]: row block rq, feature block 4 w + fs.
+  auto fs_write_p = [&](const PTile& pt) {
+    LDS_AS i32x4_t* dst = (LDS_AS i32x4_t*)(pbuf + wave * 2048 + lane * 32);
+    dst[0] = i32x4_t{pt.pb[0], pt.pb[1], pt.pb[2], pt.pb[3]};
+    dst[1] = i32x4_t{pt.pb[4], pt.pb[5], pt.pb[6], pt.pb[7]};
+    if (h == 0) scbuf[wave * 32 + l32] = pt.sc;
+  };
+  auto fs_read_p = [&](int rq, i32x8_t& pb, int& sc) {
+    const LDS_AS i32x4_t* src = (const LDS_AS i32x4_t*)(pbuf + rq * 2048 + lane * 32);
+    const i32x4_t a = src[0], c = src[1];
+    pb = i32x8_t{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+    sc = scbuf[rq * 32 + l32];
+  };
+  auto fs_pv_mfma = [&](int rq, int fs, const i32x8_t& vt, const i32x8_t& pb, int sc) {
+    oacc[4 * rq + fs] =
+        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vt, pb, oacc[4 * rq + fs], 0, 0, 0, 127, 0, sc);
+  };
+  // V^T operand of this wave's feature block fs.
+  auto fs_ld_v = [&](const LDS_AS uint8_t* tile, int fs) -> i32x8_t {
+    if constexpr (FS) return ld_pv(tile, 4 * wave + fs);
+    else return i32x8_t{};
+  };
+  // PV of a whole tile from the P tiles in LDS (the last tile).
+  auto fs_pv_tile = [&](const LDS_AS uint8_t* tv) {
+    i32x8_t vt[4], pbq[2];
+    int scq[2];
+#pragma unroll
+    for (int f = 0; f < 4; f++) vt[f] = fs_ld_v(tv, f);
+    fs_read_p(0, pbq[0], scq[0]);
+#pragma unroll
+    for (int n = 0; n < 16; n++) {
+      const int rq = n >> 2, f = n & 3;
+      if (f == 0 && rq + 1 < 4) fs_read_p(rq + 1, pbq[(rq + 1) & 1], scq[(rq + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      fs_pv_mfma(rq, f, vt[f], pbq[rq & 1], scq[rq & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // One step of the pipelined loop with the feature split: QK of tile i+1
+  // (own rows) with the DMA spread between its products, then the PV of
+  // tile i (all rows, own features) with the softmax of tile i+1 in stages
+  // between its products; the new P tile is published after every wave has
+  // read the old one.
+  auto pipe_step_fs = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped,
+                          auto mask_c) __attribute__((always_inline)) {
+    constexpr bool mask = decltype(mask_c)::value;
+    wait_vmcnt<NI * (NS - 3)>();
+    wait_lgkm0();      // this wave's P tile of tile i is in LDS
+    lds_barrier();     // tile i+1 resident; slot i-1 free; every P tile of tile i published
+    const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
+    const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
+    const int nxt = i + NS - 1;
+    const DmaSrc src = dma_prepare(nxt);
+    constexpr int DSTRIDE = NQK / NI;
+    opnd_t qa[3];
+    i32x8_t vt[4], pbq[2];
+    int scq[2];
+    qa[0] = ld_qk(tq, 0);
+    qa[1] = ld_qk(tq, 1);
+#pragma unroll
+    for (int n = 0; n < NQK; n++) {
+      if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(tq, n + 2);
+      if (n >= NQK - 4) vt[n - (NQK - 4)] = fs_ld_v(tv, n - (NQK - 4));
+      if (n == NQK - 1) fs_read_p(0, pbq[0], scq[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      qk_mfma(sacc, n, qa[n % 3]);
+      if (n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    drain_scores(sacc);
+    PTile pn;
+    SmState st;
+#pragma unroll
+    for (int n = 0; n < 16; n++) {
+      const int rq = n >> 2, f = n & 3;
+      if (f == 0 && rq + 1 < 4) fs_read_p(rq + 1, pbq[(rq + 1) & 1], scq[(rq + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      fs_pv_mfma(rq, f, vt[f], pbq[rq & 1], scq[rq & 1]);
+      sm_stage(n, mask, sacc, i + 1, jumped, st, pn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    row_sum_mfma(pt);
+    lds_barrier();     // every wave has read the P tiles of tile i
+    fs_write_p(pn);
+    pt = pn;
+  };
+
   // bf16 form of the step: its query operand takes 144 VGPRs, which leaves
   // no room to keep scores live across the PV products.  QK of tile i+1 and
   // PV of tile i alternate product by product instead, and the (short)
@@ -793,7 +897,11 @@ mla_partial_kernel(const PartialParams p) {
         softmax_all(sacc, 0, jumped, pt);
 
         int i = 0;
-        if constexpr (FP8) {
+        if constexpr (FS) {
+          fs_write_p(pt);
+          for (; i + 1 < n_clean; i++) pipe_step_fs(i, sacc, pt, jumped, std::false_type{});
+          for (; i + 1 < n_tiles; i++) pipe_step_fs(i, sacc, pt, jumped, std::true_type{});
+        } else if constexpr (FP8) {
           for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, std::false_type{});
           for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, std::true_type{});
         } else {
@@ -802,7 +910,12 @@ mla_partial_kernel(const PartialParams p) {
         }
 
         // Last tile: PV only.
-        {
+        if constexpr (FS) {
+          wait_lgkm0();
+          lds_barrier();   // every P tile of the last tile published
+          fs_pv_tile(lds + ((n_tiles - 1) % NS) * kTileBytes);
+          row_sum_mfma(pt);
+        } else {
           const LDS_AS uint8_t* tv = lds + ((n_tiles - 1) % NS) * kTileBytes;
           opnd_t va[3];
           va[0] = ld_pv(tv, 0);
@@ -877,44 +990,66 @@ mla_partial_kernel(const PartialParams p) {
   const bool empty = !(l_f > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_q;
   const float lse_v = empty ? -INFINITY : (m_ref - off + __builtin_amdgcn_logf(l_f)) * kLn2;
-  if (!row_ok) return;
-  if (p.S == 1) {
-    if (p.out_f32) {
-      float* o = (float*)p.out + qrow * 512;
+
+  // This lane's 16 values of output feature block fb of query row qr (the
+  // C layout: register 4a+c holds feature 32 fb + 8a + 4h + c).
+  auto store_block = [&](int64_t qr, int fb, const f32x16_t& acc, float iv) {
+    if (p.S == 1) {
+      if (p.out_f32) {
+        float* o = (float*)p.out + qr * 512;
 #pragma unroll
-      for (int fb = 0; fb < 16; fb++)
-#pragma unroll
-        for (int a = 0; a < 4; a++) {
-          const int f0 = 32 * fb + 8 * a + 4 * h;
-          float4 w = {oacc[fb][4 * a] * inv, oacc[fb][4 * a + 1] * inv, oacc[fb][4 * a + 2] * inv,
-                      oacc[fb][4 * a + 3] * inv};
-          *(float4*)(o + f0) = w;
+        for (int a4 = 0; a4 < 4; a4++) {
+          const float4 w = {acc[4 * a4] * iv, acc[4 * a4 + 1] * iv, acc[4 * a4 + 2] * iv, acc[4 * a4 + 3] * iv};
+          *(float4*)(o + 32 * fb + 8 * a4 + 4 * h) = w;
         }
-    } else {
-      __bf16* o = (__bf16*)p.out + qrow * 512;
-      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      } else {
+        __bf16* o = (__bf16*)p.out + qr * 512;
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
-      for (int fb = 0; fb < 16; fb++)
-#pragma unroll
-        for (int a = 0; a < 4; a++) {
-          const int f0 = 32 * fb + 8 * a + 4 * h;
-          bf16x4_t w = {(__bf16)(oacc[fb][4 * a] * inv), (__bf16)(oacc[fb][4 * a + 1] * inv),
-                        (__bf16)(oacc[fb][4 * a + 2] * inv), (__bf16)(oacc[fb][4 * a + 3] * inv)};
-          *(bf16x4_t*)(o + f0) = w;
+        for (int a4 = 0; a4 < 4; a4++) {
+          const bf16x4_t w = {(__bf16)(acc[4 * a4] * iv), (__bf16)(acc[4 * a4 + 1] * iv),
+                              (__bf16)(acc[4 * a4 + 2] * iv), (__bf16)(acc[4 * a4 + 3] * iv)};
+          *(bf16x4_t*)(o + 32 * fb + 8 * a4 + 4 * h) = w;
         }
-    }
-    if (h == 0 && p.lse) p.lse[qrow] = lse_v;
-  } else {
-    float* w = p.ws + (qrow * p.S + split) * (int64_t)kPartialWidth;
-#pragma unroll
-    for (int fb = 0; fb < 16; fb++)
-#pragma unroll
-      for (int a = 0; a < 4; a++) {
-        const int f0 = 32 * fb + 8 * a + 4 * h;
-#pragma unroll
-        for (int c = 0; c < 4; c++) w[f0 + c] = oacc[fb][4 * a + c] * inv;
       }
-    if (h == 0) w[512] = lse_v;
+    } else {
+      float* w = p.ws + (qr * p.S + split) * (int64_t)kPartialWidth + 32 * fb + 4 * h;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; a4++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) w[8 * a4 + c] = acc[4 * a4 + c] * iv;
+    }
+  };
+  auto store_lse = [&]() {
+    if (h != 0 || !row_ok) return;
+    if (p.S == 1) {
+      if (p.lse) p.lse[qrow] = lse_v;
+    } else {
+      p.ws[(qrow * p.S + split) * (int64_t)kPartialWidth + 512] = lse_v;
+    }
+  };
+
+  if constexpr (FS) {
+    // Row block rq's normalizer lives in wave rq; pass them through LDS
+    // (the P tiles are dead by now).
+    LDS_AS float* invbuf = (LDS_AS float*)pbuf;
+    if (h == 0) invbuf[wave * 32 + l32] = inv;
+    __syncthreads();
+#pragma unroll
+    for (int rq = 0; rq < 4; rq++) {
+      const int rrow = rb * (32 * RG) + rq * 32 + l32;
+      if (rrow >= p.R) continue;
+      const float iv = invbuf[rq * 32 + l32];
+      const int64_t qr = (int64_t)b * p.R + rrow;
+#pragma unroll
+      for (int f = 0; f < 4; f++) store_block(qr, 4 * wave + f, oacc[4 * rq + f], iv);
+    }
+    store_lse();
+  } else {
+    if (!row_ok) return;
+#pragma unroll
+    for (int fb = 0; fb < 16; fb++) store_block(qrow, fb, oacc[fb], inv);
+    store_lse();
   }
 }
 
@@ -971,10 +1106,10 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(const MergeParams p) {
 
 // ---------------------------------------------------------------------------
 // Launchers.
-template <bool FP8, bool SPARSE, int RG, int NS, bool RESID = false>
+template <bool FP8, bool SPARSE, int RG, int NS, bool RESID = false, bool FS = false>
 static hipError_t launch_partial(const PartialParams& p, int grid, hipStream_t stream) {
   void* args[] = {(void*)&p};
-  return hipLaunchKernel((const void*)&mla_partial_kernel<FP8, SPARSE, RG, NS, RESID>, dim3(grid), dim3(64 * RG),
+  return hipLaunchKernel((const void*)&mla_partial_kernel<FP8, SPARSE, RG, NS, RESID, FS>, dim3(grid), dim3(64 * RG),
                          args, 0, stream);
 }
 
@@ -991,7 +1126,7 @@ hipError_t launch_partial_kernel(const PartialParams& p, bool fp8, bool sparse, 
       switch (rg) {
         case 1: return launch_partial<true, false, 1, 2>(p, grid, stream);
         case 2: return launch_partial<true, false, 2, 2>(p, grid, stream);
-        case 4: return launch_partial<true, false, 4, 4>(p, grid, stream);
+        case 4: return launch_partial<true, false, 4, 4, false, true>(p, grid, stream);
       }
     }
   } else if (!fp8 && !sparse) {
