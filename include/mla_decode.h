@@ -54,7 +54,7 @@
  *    enqueued: bad dims, T outside [1, 8], block_size != 64, a NULL required
  *    pointer, num_kv_splits outside [0, MLA_MAX_KV_SPLITS], a workspace
  *    smaller than mla_workspace_size().  A split may cover at most 1024
- *    pages (dense) or 2048 top-k entries (sparse); an explicit num_kv_splits
+ *    pages (dense) or 1024 top-k entries (sparse); an explicit num_kv_splits
  *    that violates this returns MLA_ERR_UNSUPPORTED (the library's own choice
  *    never does).  A failed launch returns MLA_ERR_HIP.
  *  - Device data is not validated on the host.  In the kernels, seq_lens are
@@ -105,11 +105,13 @@ enum { MLA_OUT_BF16 = 0, MLA_OUT_F32 = 1 };
 const char* mla_status_string(mla_status_t status);
 
 /*
- * Split count the library picks for a call when num_kv_splits = 0.  It fills
- * the chip's compute units with (sequence, row block, split) work units and
- * splits further only while the split partials stay a small fraction of the
- * KV bytes.  Deterministic in its arguments; topk = 0 means a dense call,
- * otherwise a sparse call with that K.  Returns 0 on invalid arguments.
+ * Split count the library picks for a call when num_kv_splits = 0.  Work
+ * units are (sequence, row block, split).  Each candidate row-block width
+ * and split count is costed as the bytes it moves (the KV once per row block,
+ * plus the fp32 partials written and read back when split) divided by how
+ * fully its units occupy the chip's workgroup slots; the cheapest wins.
+ * Deterministic in its arguments; topk = 0 means a dense call, otherwise a
+ * sparse call with that K.  Returns 0 on invalid arguments.
  */
 int mla_num_kv_splits(int batch, int q_len, int num_heads, int max_seq_len, int topk,
                       int kv_fp8);

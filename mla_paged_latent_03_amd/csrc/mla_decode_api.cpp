@@ -39,42 +39,49 @@ bool dims_ok(int B, int T, int H, int max_seq_len, int topk) {
          max_seq_len >= 0 && max_seq_len <= (1 << 26) && topk >= 0 && topk <= (1 << 24);
 }
 
-// Split planning.  Work unit = (sequence, row block, split).  Fill the chip's
-// resident workgroup slots once; split KV only while the fp32 partials
-// (written and read back) stay under 1/16 of the KV bytes they summarize;
-// when that limit leaves slots idle, cut the rows into narrower blocks
-// instead (their KV re-reads are served from the shared L2 of one XCD).
+// Split planning.  Work unit = (sequence, row block, split).  Every
+// candidate (row-block width, split count) is costed as the bytes it moves
+// divided by how well its units fill the chip's resident workgroup slots
+// (whole rounds of units, so a last partial round counts as idle slots):
+//   bytes = KV bytes x row blocks (each row block reads its sequence's KV)
+//         + fp32 partials written and read back (when split).
+// The cheapest candidate wins; ties go to fewer splits, then wider blocks.
 bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req_splits, Plan* pl) {
   if (!dims_ok(B, T, H, max_seq_len, topk) || req_splits < 0 || req_splits > MLA_MAX_KV_SPLITS) return false;
   Plan p;
   p.R = T * H;
   const bool sparse = topk > 0;
   const int rows_blk = sparse ? H : p.R;                    // rows sharing one token list
+  const int64_t lists = (int64_t)B * (sparse ? T : 1);      // token lists (one per sequence or per draft token)
   const double kv_token_bytes = MLA_TOKEN_DIM * (fp8 ? 1.0 : 2.0);
-  // Tokens of a split one sequence reads, and the most splits that pays for itself.
   const int64_t tokens = sparse ? (int64_t)topk : (int64_t)max_seq_len;
-  const double part_bytes = (double)rows_blk * kPartialWidth * 4.0 * 2.0;  // write + read
-  const int64_t min_tokens_per_split = (int64_t)std::ceil(16.0 * part_bytes / kv_token_bytes);
-  int s_ovh = (int)(tokens / (min_tokens_per_split > 0 ? min_tokens_per_split : 1));
-  if (s_ovh < 1) s_ovh = 1;
-  // A split's index / page table lives in LDS, which bounds its length.
-  const int s_min = sparse ? ceil_div(topk, kSparseChunkMax)
-                           : ceil_div(ceil_div(max_seq_len, MLA_BLOCK_SIZE), kDensePagesMax);
+  const double kv_bytes = (double)lists * (double)tokens * kv_token_bytes;
+  const double part_bytes = (double)B * p.R * kPartialWidth * 4.0 * 2.0;   // per split: write + read
+  // A split's index / page table lives in LDS, which bounds its length from
+  // below; a split holds at least one page (dense) or one tile of indices.
+  const int max_pages = ceil_div(max_seq_len, MLA_BLOCK_SIZE);
+  const int s_min = sparse ? ceil_div(topk, kSparseChunkMax) : ceil_div(max_pages, kDensePagesMax);
+  int s_max = sparse ? ceil_div(topk, 64) : max_pages;
+  if (s_max > MLA_MAX_KV_SPLITS) s_max = MLA_MAX_KV_SPLITS;
+  if (s_max < 1) s_max = 1;
 
-  int rg = rg_for_rows(rows_blk);
-  int S = 1;
-  for (;;) {
-    const int rb_rows = 32 * rg;
-    const int n_blk = ceil_div(rows_blk, rb_rows);
-    const int64_t units = (int64_t)B * (sparse ? T : 1) * n_blk;
-    const int64_t slots = (int64_t)kNumCUs * wg_per_cu(rg);
-    const int s_fill = units > 0 ? ceil_div(slots, units) : 1;
-    S = s_fill < s_ovh ? s_fill : s_ovh;
-    if (s_fill <= s_ovh || rg == 1) break;
-    rg >>= 1;
+  int rg = rg_for_rows(rows_blk), S = 1;
+  double best = -1.0;
+  for (int g = rg_for_rows(rows_blk); g >= 1; g >>= 1) {
+    const int64_t n_blk = ceil_div(rows_blk, 32 * g);
+    const int64_t slots = (int64_t)kNumCUs * wg_per_cu(g);
+    for (int s = s_min < 1 ? 1 : s_min; s <= (s_max > s_min ? s_max : s_min); s++) {
+      const int64_t units = lists * n_blk * s;
+      if (units <= 0) break;
+      const double fill = (double)units / (double)(slots * ((units + slots - 1) / slots));
+      const double cost = (kv_bytes * (double)n_blk + (s > 1 ? part_bytes * s : 0.0)) / fill;
+      if (best < 0.0 || cost < best * 0.98) {   // a new choice must be clearly cheaper
+        best = cost;
+        rg = g;
+        S = s;
+      }
+    }
   }
-  if (S < 1) S = 1;
-  if (S > MLA_MAX_KV_SPLITS) S = MLA_MAX_KV_SPLITS;
   if (req_splits > 0) S = req_splits;
   if (S < s_min) {
     if (req_splits > 0) return false;   // the split would exceed the LDS table

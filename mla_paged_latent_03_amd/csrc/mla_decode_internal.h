@@ -10,7 +10,7 @@ constexpr int kRopeDim = 64;
 constexpr int kTokenDim = 576;
 constexpr int kPage = 64;
 constexpr int kPartialWidth = kLatentDim + 1;   // normalized outputs, then the chunk's lse
-constexpr int kSparseChunkMax = 2048;           // top-k entries one workgroup handles
+constexpr int kSparseChunkMax = 1024;           // top-k entries one workgroup handles
 constexpr int kDensePagesMax = 1024;            // pages one workgroup handles (65536 tokens)
 constexpr int kNumCUs = 256;                    // MI355X compute units
 

@@ -69,11 +69,16 @@ def test_workspace_matches_split_count(lib, B, T, H, L, K, fp8):
 def test_heuristic_fills_the_chip(lib):
     # The 80k-token MTP-3 fp8 batch: 64 sequences x 1 row block -> 4 splits = 256 workgroups.
     assert binding.num_kv_splits(64, 4, 32, 80000, 0, True) == 4
-    # One split whenever the splits' partials would cost more than they save.
-    assert binding.num_kv_splits(2, 1, 16, 300, 0, False) == 1
-    assert binding.num_kv_splits(64, 1, 128, 65536, 2048, False) == 1
+    # 128 one-wave sequences: 4 splits = 512 workgroups, two per compute unit.
+    assert binding.num_kv_splits(128, 1, 16, 8192, 0, False) == 4
+    # Sparse top-2048 over 64 sequences: 4 splits of 512 indices = 256 four-wave workgroups
+    # (narrower row blocks would read every gathered row once per block).
+    assert binding.num_kv_splits(64, 1, 128, 65536, 2048, False) == 4
+    # A chip already full of units takes one split: partials would only add traffic.
+    assert binding.num_kv_splits(256, 4, 32, 700, 0, False) == 1
+    assert binding.num_kv_splits(32, 8, 128, 32768, 0, False) == 1
     # A top-k list longer than one workgroup's index table forces splits.
-    assert binding.num_kv_splits(1, 1, 16, 10000, 5000, False) >= 3
+    assert binding.num_kv_splits(1, 1, 16, 10000, 5000, False) >= 5
 
 
 def test_launch_waves_follow_the_row_block_rules(lib):
@@ -81,10 +86,10 @@ def test_launch_waves_follow_the_row_block_rules(lib):
     assert binding.launch_waves(64, 4, 32, 80000, 0, True) == 4
     assert binding.launch_waves(32, 8, 128, 32768, 0, False) == 4
     assert binding.launch_waves(256, 1, 128, 300, 0, False) == 4
+    assert binding.launch_waves(64, 1, 128, 65536, 2048, False) == 4
     # 16 rows per sequence fit one wave.
     assert binding.launch_waves(128, 1, 16, 8192, 0, False) == 1
-    # Few short units: narrower row blocks fill the chip instead of splits.
-    assert binding.launch_waves(2, 1, 128, 300, 0, False) == 1
+    # Few short sequences: narrower row blocks (and splits) fill more of the chip.
     assert binding.launch_waves(4, 1, 64, 300, 0, False) == 1
     # 64 rows and units enough for two workgroups per compute unit: two waves.
     assert binding.launch_waves(512, 1, 64, 300, 0, False) == 2
