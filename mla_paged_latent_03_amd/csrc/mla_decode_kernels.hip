@@ -189,6 +189,14 @@ __device__ inline void mfma_bf16_first(f32x16_t& acc, const bf16x8_t& a, const b
 __device__ inline void mfma_bf16_acc(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+// Keeps the computation of a value at this point of the program: an empty
+// inline-asm use.  Softmax stages produce values that are only consumed at
+// the end of a loop step; without this, IR-level sinking moves their
+// arithmetic down to that use, past the scheduling barriers that are meant
+// to interleave it with matrix products.
+__device__ inline void pin(int& x) { asm volatile("" : "+v"(x)); }
+__device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 // 24 wait states after the last product of a chain.  The accumulators are
 // in/out operands: code that reads them then depends on this statement and
 // cannot be scheduled above the padding (with no operands the compiler is
@@ -224,7 +232,7 @@ mla_partial_kernel(const PartialParams p) {
   static_assert(!FS || (FP8 && !SPARSE && RG == 4 && !RESID), "feature split: dense fp8, four waves");
   constexpr int kTableCap = SPARSE ? kSparseChunkMax : kDensePagesMax;
   constexpr int kPBytes = FS ? 4 * 2048 : 0;      // FS: P tile of each row block (64 lanes x 32 B)
-  constexpr int kScBytes = FS ? 4 * 32 * 4 : 0;   // FS: E8M0 scale of each row of the block
+  constexpr int kScBytes = FS ? 4 * 64 * 4 : 0;   // FS: E8M0 scales of each row block (per lane)
 
   // LDS: [ring of NS tiles][unit table: int32 x kTableCap][FS: P tiles][FS: scales][redo flag]
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kTileBytes + kTableCap * 4 + kPBytes + kScBytes + 16];
@@ -452,7 +460,7 @@ mla_partial_kernel(const PartialParams p) {
   typedef typename std::conditional<FP8, i32x8_t, bf16x8_t>::type opnd_t;
   auto ld_qk = [&](const LDS_AS uint8_t* tile, int n) -> opnd_t {
     if constexpr (FP8) {
-      const LDS_AS uint8_t* base = tile + (n & 1) * 32 * K::kRowBytes + 64 * (n >> 1);
+      const LDS_AS uint8_t* base = tile + (n / K::kQkSteps) * 32 * K::kRowBytes + 64 * (n % K::kQkSteps);
       const i32x4_t lo = *(const LDS_AS i32x4_t*)(base + a_off[0]);
       const i32x4_t hi = *(const LDS_AS i32x4_t*)(base + a_off[1]);
       return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -508,7 +516,7 @@ mla_partial_kernel(const PartialParams p) {
   // QK product n on accumulator sacc (VGPR chain).
   auto qk_mfma = [&](f32x16_t (&sacc)[K::kTokBlocks], int n, const opnd_t& a) {
     if constexpr (FP8) {
-      const int k = n >> 1, tb = n & 1;
+      const int k = n % K::kQkSteps, tb = n / K::kQkSteps;   // token block 0's chain first
       const i32x8_t bq = {qreg[8 * k], qreg[8 * k + 1], qreg[8 * k + 2], qreg[8 * k + 3],
                           qreg[8 * k + 4], qreg[8 * k + 5], qreg[8 * k + 6], qreg[8 * k + 7]};
       if (k == 0) mfma_f8_first(sacc[tb], a, bq, e8m0_one, e8m0_one);
@@ -553,129 +561,148 @@ mla_partial_kernel(const PartialParams p) {
     else mfma_drain(sacc[0]);
   };
 
-  // ---- softmax of one tile, in stages.  The pipelined loop places the
-  // stages between the PV products of the previous tile, so that their
-  // VALU work runs while the matrix core is busy.
+  // ---- softmax of one tile, in stages, token block by token block.  The
+  // pipelined loops place the stages of token block 0 between the QK
+  // products of block 1 and those of block 1 between the PV products of the
+  // previous tile, so that their VALU work runs while the matrix core is busy.
   //
   // Register v of token block tb holds token 32*tb + 8*(v/4) + 4*h + v%4.
-  constexpr int NEXP = FP8 ? 8 : 4;      // exponent stages, four scores each
+  // fp8: each token block carries its own E8M0 scale.  In the P operand,
+  // bytes 0-15 of both wave halves are token block 0 and bytes 16-31 token
+  // block 1, and the MFMA applies lane j's B scale to the first of those
+  // K-blocks of column j and lane j+32's to the second.
+  constexpr int NEXP = 4;                // exponent stages per token block, four scores each
   struct SmState {
-    float ml;       // this lane's running maximum of the tile's scores
-    float shift;    // exponent offset applied to scaled scores
-    float psum;     // this lane's sum of the unrounded weights
+    float ml[K::kTokBlocks];     // this lane's maximum of the block's scores
+    float shift[K::kTokBlocks];  // exponent offset applied to the block's scaled scores
+    float psum[K::kTokBlocks];   // this lane's sum of the block's unrounded weights
+    int sc[K::kTokBlocks];       // fp8: E8M0 scale of the block's weights
   };
 
-  // Mask: compare each register's compile-time token offset (without the
-  // 4*h) against one per-lane limit.  Selects, not branches: a branch here
-  // splits the loop body and costs far more registers.
-  auto sm_mask = [&](f32x16_t (&sacc)[K::kTokBlocks], int i) {
+  // Mask of token block tb: compare each register's compile-time token
+  // offset (without the 4*h) against one per-lane limit.  Selects, not
+  // branches: a branch here splits the loop body and costs registers.
+  auto sm_mask = [&](f32x16_t (&sacc)[K::kTokBlocks], int i, int tb) {
     if (SPARSE) {
       const int phys = lane < K::kTileTok ? table[i * K::kTileTok + lane] : 0;
       const uint64_t valid = __builtin_amdgcn_ballot_w64(phys >= 0) | (K::kTileTok == 64 ? 0ull : ~0ull << 32);
       const uint64_t mine = valid >> (4 * h);
 #pragma unroll
-      for (int tb = 0; tb < K::kTokBlocks; tb++)
-#pragma unroll
-        for (int v = 0; v < 16; v++)
-          sacc[tb][v] = (mine >> (32 * tb + 8 * (v >> 2) + (v & 3))) & 1 ? sacc[tb][v] : -INFINITY;
+      for (int v = 0; v < 16; v++)
+        sacc[tb][v] = (mine >> (32 * tb + 8 * (v >> 2) + (v & 3))) & 1 ? sacc[tb][v] : -INFINITY;
     } else {
       const int lim = n_vis - (tok_begin + i * K::kTileTok) - 4 * h;   // offsets at or past lim are masked
 #pragma unroll
-      for (int tb = 0; tb < K::kTokBlocks; tb++)
-#pragma unroll
-        for (int v = 0; v < 16; v++)
-          sacc[tb][v] = 32 * tb + 8 * (v >> 2) + (v & 3) < lim ? sacc[tb][v] : -INFINITY;
+      for (int v = 0; v < 16; v++)
+        sacc[tb][v] = 32 * tb + 8 * (v >> 2) + (v & 3) < lim ? sacc[tb][v] : -INFINITY;
     }
   };
-  // Stage "max of token block tb".
-  auto sm_max_block = [&](f32x16_t (&sacc)[K::kTokBlocks], int tb, SmState& st) {
-    float m = tb == 0 ? -INFINITY : st.ml;
+  // Stage "lane maximum of token block tb".
+  auto sm_max = [&](f32x16_t (&sacc)[K::kTokBlocks], int tb, SmState& st) {
+    float m = sacc[tb][0];
 #pragma unroll
-    for (int v = 0; v < 16; v++) m = fmaxf(m, sacc[tb][v]);
-    st.ml = m;
+    for (int v = 1; v < 16; v++) m = fmaxf(m, sacc[tb][v]);
+    st.ml[tb] = m;
   };
-  // Stage "row maximum": reference, per-tile shift and (fp8) P scales.
-  auto sm_max_row = [&](bool& jumped, SmState& st, PTile& pt) {
-    const float ml = st.ml * c_qk;       // this lane's maximum, scaled (-inf if all masked)
+  // Stage "row maximum of token block tb": the reference (set by the first
+  // block a row sees), the block's shift and (fp8) its scale.
+  auto sm_row = [&](int tb, bool& jumped, SmState& st) {
+    const float ml = st.ml[tb] * c_qk;   // this lane's maximum, scaled (-inf if all masked)
     m_seen = fmaxf(m_seen, ml);
-    // A jump is measured against a reference already set by an earlier tile.
+    // A jump is measured against a reference already set by an earlier block.
     jumped |= m_ref != kNegBig && ml > m_ref + 64.f;
     const float mrow = max_across_halves(ml);
     if constexpr (FP8) {
       // P' = 2^(x - mi + 8) in [0, 256] -> e4m3, with mi the integer ceiling
-      // of the row's tile maximum; the PV MFMA multiplies it by 2^(mi - m_ref)
-      // through the E8M0 scale of its P operand.  (The scale must be one per
-      // row: an E8M0 K-block spans bytes of both wave halves.)
+      // of the row's block maximum; the PV MFMA multiplies it by 2^(mi - m_ref)
+      // through the block's E8M0 scale.
       if (m_ref == kNegBig && mrow != -INFINITY) m_ref = ceilf(mrow);
       const float mi = mrow == -INFINITY ? m_ref : ceilf(mrow);
-      st.shift = 8.f - mi;
+      st.shift[tb] = 8.f - mi;
       // E8M0 biased exponent of 2^(mi - m_ref), clamped to the format
-      // (0 = 2^-127: the tile's weights are negligible there).
+      // (0 = 2^-127: the block's weights are negligible there).
       const float dexp = fminf(mi - m_ref, 64.f);
-      pt.sc = dexp < -126.f ? 0 : (int)dexp + 127;
-      pt.scl = pt.sc > 4 ? pt.sc - 4 : 0;
+      st.sc[tb] = dexp < -126.f ? 0 : (int)dexp + 127;
+      pin(st.sc[tb]);
+      pin(st.shift[tb]);
     } else {
       if (m_ref == kNegBig && mrow != -INFINITY) m_ref = mrow;
-      st.shift = -m_ref;
-      pt.sc = pt.scl = 0;
+      st.shift[tb] = -m_ref;
+      st.sc[tb] = 0;
     }
-    st.psum = 0.f;
+    st.psum[tb] = 0.f;
   };
-  // Stage "exponents of registers 4d .. 4d+3" (fp8: token block d/4).
-  auto sm_exp = [&](f32x16_t (&sacc)[K::kTokBlocks], int d, SmState& st, PTile& pt) {
-    const int tb = FP8 ? d >> 2 : 0;
-    const int v = FP8 ? 4 * (d & 3) : 4 * d;
-    const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v], c_qk, st.shift));
-    const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 1], c_qk, st.shift));
-    const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 2], c_qk, st.shift));
-    const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 3], c_qk, st.shift));
-    st.psum += (e0 + e1) + (e2 + e3);
+  // Stage "exponents of registers 4d .. 4d+3 of token block tb".
+  auto sm_exp = [&](f32x16_t (&sacc)[K::kTokBlocks], int tb, int d, SmState& st, PTile& pt) {
+    const int v = 4 * d;
+    const float sh = st.shift[tb];
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v], c_qk, sh));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 1], c_qk, sh));
+    const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 2], c_qk, sh));
+    const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v + 3], c_qk, sh));
+    st.psum[tb] += (e0 + e1) + (e2 + e3);
+    pin(st.psum[tb]);
     if constexpr (FP8) {
       int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
-      pt.pb[d] = w;
+      pin(w);
+      pt.pb[4 * tb + d] = w;
       if constexpr (RESID) {
         // lo = e4m3(16 (P' - hi)): hi + lo/16 holds P' to about 2^-8.
         const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
         const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
         int wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e0 - h01[0]), 16.f * (e1 - h01[1]), 0, false);
         wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (e2 - h23[0]), 16.f * (e3 - h23[1]), wl, true);
-        pt.pbl[d] = wl;
+        pin(wl);
+        pt.pbl[4 * tb + d] = wl;
       } else {
-        pt.pbl[d] = 0;
+        pt.pbl[4 * tb + d] = 0;
       }
     } else {
       // P operand: registers 8*kk .. 8*kk+7 form k-step kk; two bf16 per dword.
       typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
       const bf16x2_t lo = {(__bf16)e0, (__bf16)e1};
       const bf16x2_t hi = {(__bf16)e2, (__bf16)e3};
-      pt.pb[2 * d] = __builtin_bit_cast(int, lo);
-      pt.pb[2 * d + 1] = __builtin_bit_cast(int, hi);
+      int wlo = __builtin_bit_cast(int, lo), whi = __builtin_bit_cast(int, hi);
+      pin(wlo);
+      pin(whi);
+      pt.pb[2 * d] = wlo;
+      pt.pb[2 * d + 1] = whi;
     }
   };
-  // Stage "finish": this half's unrounded weights join l_f.
-  auto sm_finish = [&](const SmState& st, const PTile& pt) {
-    if constexpr (FP8) l_f += st.psum * __builtin_amdgcn_ldexpf(1.0f, pt.sc - 127);
-    else l_f += st.psum;
+  // Stage "finish": the P operand's scales (lane half h carries token
+  // block h's) and this half's unrounded weights join l_f.
+  auto sm_finish = [&](const SmState& st, PTile& pt) {
+    if constexpr (FP8) {
+      pt.sc = h == 0 ? st.sc[0] : st.sc[1];
+      pt.scl = pt.sc > 4 ? pt.sc - 4 : 0;
+      l_f += st.psum[0] * __builtin_amdgcn_ldexpf(1.0f, st.sc[0] - 127) +
+             st.psum[1] * __builtin_amdgcn_ldexpf(1.0f, st.sc[1] - 127);
+    } else {
+      pt.sc = pt.scl = 0;
+      l_f += st.psum[0];
+    }
   };
-  // Stage k of a tile's softmax (compile-time k once loops are unrolled);
-  // returns false past the last stage.
-  constexpr int NSTAGE_CLEAN = K::kTokBlocks + 1 + NEXP + 1;
-  auto sm_stage = [&](int k, bool mask, f32x16_t (&sacc)[K::kTokBlocks], int i, bool& jumped, SmState& st,
-                      PTile& pt) {
+  // Stage k of token block tb's softmax (compile-time k once loops are
+  // unrolled): [mask], max, row, NEXP exponent stages; no-op past the end.
+  constexpr int NSTAGE_BLOCK = 2 + NEXP;
+  auto sm_block_stage = [&](int k, bool mask, f32x16_t (&sacc)[K::kTokBlocks], int i, int tb, bool& jumped,
+                            SmState& st, PTile& pt) {
     if (mask) {
-      if (k == 0) { sm_mask(sacc, i); return; }
+      if (k == 0) { sm_mask(sacc, i, tb); return; }
       k -= 1;
     }
-    if (k < K::kTokBlocks) sm_max_block(sacc, k, st);
-    else if (k == K::kTokBlocks) sm_max_row(jumped, st, pt);
-    else if (k < K::kTokBlocks + 1 + NEXP) sm_exp(sacc, k - K::kTokBlocks - 1, st, pt);
-    else if (k == K::kTokBlocks + 1 + NEXP) sm_finish(st, pt);
+    if (k == 0) sm_max(sacc, tb, st);
+    else if (k == 1) sm_row(tb, jumped, st);
+    else if (k < 2 + NEXP) sm_exp(sacc, tb, k - 2, st, pt);
   };
   auto softmax_all = [&](f32x16_t (&sacc)[K::kTokBlocks], int i, bool& jumped, PTile& pt) {
     SmState st;
 #pragma unroll
-    for (int k = 0; k < NSTAGE_CLEAN + 1; k++) sm_stage(k, true, sacc, i, jumped, st, pt);
+    for (int tb = 0; tb < K::kTokBlocks; tb++)
+#pragma unroll
+      for (int k = 0; k < NSTAGE_BLOCK + 1; k++) sm_block_stage(k, true, sacc, i, tb, jumped, st, pt);
+    sm_finish(st, pt);
   };
 
   // ---- tiles [0, n_clean) need no mask: every row sees all their tokens
@@ -687,12 +714,14 @@ mla_partial_kernel(const PartialParams p) {
     n_clean = lim0 > 0 ? min(n_tiles, lim0 / K::kTileTok) : 0;
   }
 
-  // ---- one step of the pipelined loop (four waves): QK of tile i+1 with
-  // the DMA of tile i+NS-1 spread between its products, then the softmax
-  // of tile i+1 in stages between the PV products of tile i.
+  // ---- one step of the pipelined loop (four waves, fp8): QK of tile i+1
+  // (token block 0, then block 1) with the DMA of tile i+NS-1 spread between
+  // its products and token block 0's softmax between block 1's products;
+  // then the PV products of tile i with block 1's softmax between them.
   auto pipe_step = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped,
                        auto mask_c) __attribute__((always_inline)) {
     constexpr bool mask = decltype(mask_c)::value;
+    constexpr int KS = K::kQkSteps;
     // Tile i+1 resident (one tile may still be in flight behind it); every
     // wave is done with tile i-1, whose slot the DMA below refills.
     wait_vmcnt<NI * (NS - 3)>();
@@ -704,6 +733,8 @@ mla_partial_kernel(const PartialParams p) {
     constexpr int DSTRIDE = NQK / NI;
     static_assert(NQK % NI == 0, "DMA spread");
     opnd_t qa[3], va[3];
+    PTile pn;
+    SmState st;
     qa[0] = ld_qk(tq, 0);
     qa[1] = ld_qk(tq, 1);
 #pragma unroll
@@ -713,21 +744,23 @@ mla_partial_kernel(const PartialParams p) {
       if (n == NQK - 1) va[1] = ld_pv(tv, 1);
       __builtin_amdgcn_sched_barrier(0);
       qk_mfma(sacc, n, qa[n % 3]);
+      if (n == KS) mfma_drain(sacc[0]);          // block 0's chain ended one product ago
+      if (n > KS) sm_block_stage(n - KS - 1, mask, sacc, i + 1, 0, jumped, st, pn);
       if (n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
     }
-    drain_scores(sacc);
-    PTile pn;
-    SmState st;
+    static_assert(NSTAGE_BLOCK + 1 <= KS - 1, "block 0's stages fit between block 1's products");
 #pragma unroll
     for (int n = 0; n < NPV; n++) {
       if (n + 2 < NPV) va[(n + 2) % 3] = ld_pv(tv, n + 2);
       __builtin_amdgcn_sched_barrier(0);
       pv_mfma(n, va[n % 3], pt);
-      sm_stage(n, mask, sacc, i + 1, jumped, st, pn);
+      if (n == 0) mfma_drain(sacc[1]);
+      if (n > 0) sm_block_stage(n - 1, mask, sacc, i + 1, 1, jumped, st, pn);
+      if (n == NSTAGE_BLOCK + 2) sm_finish(st, pn);
       __builtin_amdgcn_sched_barrier(0);
     }
-    static_assert(NSTAGE_CLEAN + 1 <= NPV, "softmax stages fit between the PV products");
+    static_assert(NSTAGE_BLOCK + 3 <= NPV, "block 1's stages fit between the PV products");
     row_sum_mfma(pt);
     pt = pn;
   };
@@ -737,89 +770,106 @@ mla_partial_kernel(const PartialParams p) {
   // byte of V is read from LDS by one wave instead of four.  The P tile
   // (fp8, in the B-operand layout) and the E8M0 scales of each row block
   // pass from the wave that computed them to the others through LDS.
-  // oacc[4 * rq + fs]: row block rq, feature block 4 w + fs.
+  // oacc[4 * r + fs]: row block (w + r) mod 4 (r = 0 is the wave's own),
+  // feature block 4 w + fs; r and fs are compile-time indices.
   auto fs_write_p = [&](const PTile& pt) {
     LDS_AS i32x4_t* dst = (LDS_AS i32x4_t*)(pbuf + wave * 2048 + lane * 32);
     dst[0] = i32x4_t{pt.pb[0], pt.pb[1], pt.pb[2], pt.pb[3]};
     dst[1] = i32x4_t{pt.pb[4], pt.pb[5], pt.pb[6], pt.pb[7]};
-    if (h == 0) scbuf[wave * 32 + l32] = pt.sc;
+    scbuf[wave * 64 + lane] = pt.sc;       // lane half h: token block h's scale
   };
   auto fs_read_p = [&](int rq, i32x8_t& pb, int& sc) {
     const LDS_AS i32x4_t* src = (const LDS_AS i32x4_t*)(pbuf + rq * 2048 + lane * 32);
     const i32x4_t a = src[0], c = src[1];
     pb = i32x8_t{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
-    sc = scbuf[rq * 32 + l32];
+    sc = scbuf[rq * 64 + lane];
   };
-  auto fs_pv_mfma = [&](int rq, int fs, const i32x8_t& vt, const i32x8_t& pb, int sc) {
-    oacc[4 * rq + fs] =
-        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vt, pb, oacc[4 * rq + fs], 0, 0, 0, 127, 0, sc);
+  auto fs_pv_mfma = [&](int r, int fs, const i32x8_t& vt, const i32x8_t& pb, int sc) {
+    oacc[4 * r + fs] =
+        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vt, pb, oacc[4 * r + fs], 0, 0, 0, 127, 0, sc);
   };
   // V^T operand of this wave's feature block fs.
   auto fs_ld_v = [&](const LDS_AS uint8_t* tile, int fs) -> i32x8_t {
     if constexpr (FS) return ld_pv(tile, 4 * wave + fs);
     else return i32x8_t{};
   };
-  // PV of a whole tile from the P tiles in LDS (the last tile).
-  auto fs_pv_tile = [&](const LDS_AS uint8_t* tv) {
-    i32x8_t vt[4], pbq[2];
+  // PV of a whole tile (the last one): own row block from registers, the
+  // others from the P tiles in LDS; vt holds the tile's Vᵀ operands.
+  auto fs_pv_tile = [&](const i32x8_t (&vt)[4], const PTile& pt) {
+    i32x8_t pbq[2];
     int scq[2];
+    fs_read_p((wave + 1) & 3, pbq[0], scq[0]);
 #pragma unroll
-    for (int f = 0; f < 4; f++) vt[f] = fs_ld_v(tv, f);
-    fs_read_p(0, pbq[0], scq[0]);
+    for (int f = 0; f < 4; f++) fs_pv_mfma(0, f, vt[f], pt.pb, pt.sc);
 #pragma unroll
-    for (int n = 0; n < 16; n++) {
-      const int rq = n >> 2, f = n & 3;
-      if (f == 0 && rq + 1 < 4) fs_read_p(rq + 1, pbq[(rq + 1) & 1], scq[(rq + 1) & 1]);
+    for (int n = 0; n < 12; n++) {
+      const int j = n >> 2, f = n & 3;
+      if (f == 0 && j + 1 < 3) fs_read_p((wave + 2 + j) & 3, pbq[(j + 1) & 1], scq[(j + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      fs_pv_mfma(rq, f, vt[f], pbq[rq & 1], scq[rq & 1]);
+      fs_pv_mfma(1 + j, f, vt[f], pbq[j & 1], scq[j & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // One step of the pipelined loop with the feature split: QK of tile i+1
-  // (own rows) with the DMA spread between its products, then the PV of
-  // tile i (all rows, own features) with the softmax of tile i+1 in stages
-  // between its products; the new P tile is published after every wave has
-  // read the old one.
-  auto pipe_step_fs = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped,
+  // One step of the pipelined loop with the feature split.  Right after the
+  // barrier the wave runs the PV products of its own row block, whose
+  // operands are already in registers (its own P tile, and this tile's Vᵀ
+  // loaded at the end of the previous step), while the QK operands of tile
+  // i+1 arrive from LDS.  Then QK of tile i+1 (token block 0, then block 1)
+  // with the DMA spread between its products and block 0's softmax between
+  // block 1's products; then the PV of the other row blocks with block 1's
+  // softmax between them.  The new P tile is published after every wave has
+  // read the old one, and the next tile's Vᵀ is loaded for the next step.
+  auto pipe_step_fs = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, i32x8_t (&vt)[4], bool& jumped,
                           auto mask_c) __attribute__((always_inline)) {
     constexpr bool mask = decltype(mask_c)::value;
+    constexpr int KS = K::kQkSteps;
     wait_vmcnt<NI * (NS - 3)>();
-    wait_lgkm0();      // this wave's P tile of tile i is in LDS
+    wait_lgkm0();      // this wave's P tile of tile i is in LDS, this tile's Vᵀ in registers
     lds_barrier();     // tile i+1 resident; slot i-1 free; every P tile of tile i published
-    const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
     const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
     const int nxt = i + NS - 1;
     const DmaSrc src = dma_prepare(nxt);
     constexpr int DSTRIDE = NQK / NI;
     opnd_t qa[3];
-    i32x8_t vt[4], pbq[2];
+    i32x8_t pbq[2];
     int scq[2];
+    PTile pn;
+    SmState st;
     qa[0] = ld_qk(tq, 0);
     qa[1] = ld_qk(tq, 1);
 #pragma unroll
+    for (int f = 0; f < 4; f++) {
+      __builtin_amdgcn_sched_barrier(0);
+      fs_pv_mfma(0, f, vt[f], pt.pb, pt.sc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
     for (int n = 0; n < NQK; n++) {
       if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(tq, n + 2);
-      if (n >= NQK - 4) vt[n - (NQK - 4)] = fs_ld_v(tv, n - (NQK - 4));
-      if (n == NQK - 1) fs_read_p(0, pbq[0], scq[0]);
+      if (n == NQK - 1) fs_read_p((wave + 1) & 3, pbq[0], scq[0]);
       __builtin_amdgcn_sched_barrier(0);
       qk_mfma(sacc, n, qa[n % 3]);
+      if (n == KS) mfma_drain(sacc[0]);          // block 0's chain ended one product ago
+      if (n > KS) sm_block_stage(n - KS - 1, mask, sacc, i + 1, 0, jumped, st, pn);
       if (n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
     }
-    drain_scores(sacc);
-    PTile pn;
-    SmState st;
 #pragma unroll
-    for (int n = 0; n < 16; n++) {
-      const int rq = n >> 2, f = n & 3;
-      if (f == 0 && rq + 1 < 4) fs_read_p(rq + 1, pbq[(rq + 1) & 1], scq[(rq + 1) & 1]);
+    for (int n = 0; n < 12; n++) {
+      const int j = n >> 2, f = n & 3;
+      if (f == 0 && j + 1 < 3) fs_read_p((wave + 2 + j) & 3, pbq[(j + 1) & 1], scq[(j + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      fs_pv_mfma(rq, f, vt[f], pbq[rq & 1], scq[rq & 1]);
-      sm_stage(n, mask, sacc, i + 1, jumped, st, pn);
+      fs_pv_mfma(1 + j, f, vt[f], pbq[j & 1], scq[j & 1]);
+      if (n == 0) mfma_drain(sacc[1]);
+      if (n > 0) sm_block_stage(n - 1, mask, sacc, i + 1, 1, jumped, st, pn);
+      if (n == NSTAGE_BLOCK + 2) sm_finish(st, pn);
       __builtin_amdgcn_sched_barrier(0);
     }
+    static_assert(NSTAGE_BLOCK + 3 <= 12, "block 1's stages fit between the other row blocks' products");
     row_sum_mfma(pt);
     lds_barrier();     // every wave has read the P tiles of tile i
+#pragma unroll
+    for (int f = 0; f < 4; f++) vt[f] = fs_ld_v(tq, f);   // Vᵀ of tile i+1 for the next step
     fs_write_p(pn);
     pt = pn;
   };
@@ -856,7 +906,8 @@ mla_partial_kernel(const PartialParams p) {
     drain_scores(sacc);
     SmState st;
 #pragma unroll
-    for (int k = 0; k < NSTAGE_CLEAN + 1; k++) sm_stage(k, mask, sacc, i + 1, jumped, st, pt);
+    for (int k = 0; k < NSTAGE_BLOCK + 1; k++) sm_block_stage(k, mask, sacc, i + 1, 0, jumped, st, pt);
+    sm_finish(st, pt);
   };
 
   // ---- the tile loop, at most twice (second pass: exact reference)
@@ -897,10 +948,13 @@ mla_partial_kernel(const PartialParams p) {
         softmax_all(sacc, 0, jumped, pt);
 
         int i = 0;
+        i32x8_t vt[4];   // FS: Vᵀ operands of the tile whose PV comes next (own features)
         if constexpr (FS) {
           fs_write_p(pt);
-          for (; i + 1 < n_clean; i++) pipe_step_fs(i, sacc, pt, jumped, std::false_type{});
-          for (; i + 1 < n_tiles; i++) pipe_step_fs(i, sacc, pt, jumped, std::true_type{});
+#pragma unroll
+          for (int f = 0; f < 4; f++) vt[f] = fs_ld_v(lds, f);
+          for (; i + 1 < n_clean; i++) pipe_step_fs(i, sacc, pt, vt, jumped, std::false_type{});
+          for (; i + 1 < n_tiles; i++) pipe_step_fs(i, sacc, pt, vt, jumped, std::true_type{});
         } else if constexpr (FP8) {
           for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, std::false_type{});
           for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, std::true_type{});
@@ -913,7 +967,7 @@ mla_partial_kernel(const PartialParams p) {
         if constexpr (FS) {
           wait_lgkm0();
           lds_barrier();   // every P tile of the last tile published
-          fs_pv_tile(lds + ((n_tiles - 1) % NS) * kTileBytes);
+          fs_pv_tile(vt, pt);
           row_sum_mfma(pt);
         } else {
           const LDS_AS uint8_t* tv = lds + ((n_tiles - 1) % NS) * kTileBytes;
@@ -1036,13 +1090,14 @@ mla_partial_kernel(const PartialParams p) {
     if (h == 0) invbuf[wave * 32 + l32] = inv;
     __syncthreads();
 #pragma unroll
-    for (int rq = 0; rq < 4; rq++) {
+    for (int r = 0; r < 4; r++) {
+      const int rq = (wave + r) & 3;
       const int rrow = rb * (32 * RG) + rq * 32 + l32;
       if (rrow >= p.R) continue;
       const float iv = invbuf[rq * 32 + l32];
       const int64_t qr = (int64_t)b * p.R + rrow;
 #pragma unroll
-      for (int f = 0; f < 4; f++) store_block(qr, 4 * wave + f, oacc[4 * rq + f], iv);
+      for (int f = 0; f < 4; f++) store_block(qr, 4 * wave + f, oacc[4 * r + f], iv);
     }
     store_lse();
   } else {
