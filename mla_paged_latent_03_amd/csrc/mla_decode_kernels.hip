@@ -117,18 +117,6 @@ __device__ inline void wait_lgkm0() {
   asm volatile("" ::: "memory");
 }
 
-template <int NI, int MAXR>
-__device__ inline void wait_tiles_after(int remaining) {
-  // Wait until at most `remaining` tiles (NI loads each) are still in flight.
-  if constexpr (MAXR >= 2) {
-    if (remaining >= 2) { wait_vmcnt<2 * NI>(); return; }
-  }
-  if constexpr (MAXR >= 1) {
-    if (remaining >= 1) { wait_vmcnt<NI>(); return; }
-  }
-  wait_vmcnt<0>();
-}
-
 // Combine the two halves of a wave (lanes l and l ^ 32 hold the same row)
 // with v_permlane32_swap.  Issued from inline asm: the builtin applied to
 // one value twice gets folded away by the compiler.
@@ -986,13 +974,18 @@ mla_partial_kernel(const PartialParams p) {
         wait_vmcnt<0>();   // the zero fills past the end must land before the LDS is reused
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < NS - 1; i++)
-        if (i < n_tiles) issue_tile(i, i);
+      // Two-slot loop (one or two waves): tile i+1 streams into the other
+      // slot while tile i is computed, its DMA instructions spread between
+      // the QK products (a wave can keep at most 63 vector-memory
+      // instructions in flight, so a one-wave workgroup holds one tile in
+      // flight at a time).  Past the end the slot gets a zero fill, which
+      // keeps the wait a constant.
+      static_assert(NS == 2, "two-slot loop");
+      if (n_tiles > 0) issue_tile(0, 0);
       for (int i = 0; i < n_tiles; i++) {
-        wait_tiles_after<NI, NS - 2>(min(NS - 2, n_tiles - 1 - i));
-        if (RG > 1) lds_barrier();
-        if (i + NS - 1 < n_tiles) issue_tile(i + NS - 1, (i + NS - 1) % NS);
+        wait_vmcnt<0>();
+        if (RG > 1) lds_barrier();   // tile i complete; every wave is done with tile i-1's slot
+        const DmaSrc src = dma_prepare(i + 1);
         const LDS_AS uint8_t* tile = lds + (i % NS) * kTileBytes;
         f32x16_t sacc[K::kTokBlocks];
         {
@@ -1004,6 +997,10 @@ mla_partial_kernel(const PartialParams p) {
             if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(tile, n + 2);
             __builtin_amdgcn_sched_barrier(0);
             qk_mfma(sacc, n, qa[n % 3]);
+            // DMA instructions j with floor(j * NQK / NI) == n follow product n.
+#pragma unroll
+            for (int j = (n * NI + NQK - 1) / NQK; j < ((n + 1) * NI + NQK - 1) / NQK; j++)
+              dma_issue(src, (i + 1) % NS, j);
             __builtin_amdgcn_sched_barrier(0);
           }
           drain_scores(sacc);
@@ -1022,6 +1019,7 @@ mla_partial_kernel(const PartialParams p) {
         }
         row_sum_mfma(pt);
       }
+      wait_vmcnt<0>();   // the zero fill past the end must land before the LDS is reused
     }
     mfma_drain(lsum);
 
