@@ -163,6 +163,45 @@ def test_fp8_scales_are_read_every_call():
         check_full(inp, 0, "fp8 kv_scale %.3g" % ks)
 
 
+# ------------------------------------------------------------------ edge and limit cases
+
+def test_fp8_long_units_without_residual_product():
+    """Units longer than 8192 tokens use one fp8 PV product per block (no
+    residual); with 128 rows per sequence and many sequences they run on the
+    four-wave feature-split kernel."""
+    inp = wl.make_inputs(64, 32, 4, (8500, 9500), kv_dtype="fp8", out_dtype="f32", seed=51)
+    assert binding.launch_waves(64, 4, 32, inp.max_len, 0, True) == 4
+    out, lse = run_case(inp, 1, "fp8 long units, one split")
+    rows = sample_rows(64 * 4 * 32, 96, seed=51)
+    ref_o, ref_l = oracle_rows(inp, rows=rows)
+    compare(out, lse, ref_o, ref_l, "fp8", rows=rows, what="fp8 long units")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_sequence_past_the_split_cap_is_split(kv_dtype):
+    """One split covers at most 1024 pages: a 70000-token sequence needs two,
+    the library picks at least that many, and an explicit single split is
+    refused before any launch."""
+    inp = wl.make_inputs(1, 16, 1, [70000], kv_dtype=kv_dtype, out_dtype="f32", seed=52)
+    assert binding.num_kv_splits(1, 1, 16, 70000, 0, kv_dtype == "fp8") >= 2
+    check_full(inp, 0, "70000 tokens %s" % kv_dtype)
+    with pytest.raises(binding.MLAError):
+        binding.decode(inp.to(DEV), num_kv_splits=1)
+
+
+def test_maximum_split_count_with_empty_splits():
+    """MLA_MAX_KV_SPLITS splits over a five-page sequence: most splits see no
+    token (lse -inf partials) and the merge must ignore them."""
+    inp = wl.make_inputs(2, 16, 1, [300, 70], kv_dtype="bf16", out_dtype="f32", seed=53)
+    check_full(inp, binding.MAX_KV_SPLITS, "256 splits")
+
+
+@pytest.mark.parametrize("H,T,kv_dtype", [(1, 1, "bf16"), (1, 8, "bf16"), (1, 8, "fp8"), (16, 8, "bf16")])
+def test_degenerate_head_counts_and_longest_draft(H, T, kv_dtype):
+    inp = wl.make_inputs(3, H, T, [5, 200, 1500], kv_dtype=kv_dtype, out_dtype="f32", seed=54 + H + T, poison=True)
+    check_full(inp, 0, "H=%d T=%d %s" % (H, T, kv_dtype))
+
+
 # ------------------------------------------------------------------ sparse
 
 @pytest.mark.parametrize("H,T,lens,K,splits", [
