@@ -126,6 +126,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-gib", type=int, default=0,
+                    help="first copy a buffer of this many GiB three times, so that a counter run over the "
+                         "benchmark also reads the counters for a plain copy of known size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -173,6 +176,15 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n           # ms per call
+
+    if args.copy_calibration_gib > 0:
+        src = torch.ones(args.copy_calibration_gib << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied %d GiB three times" % args.copy_calibration_gib)
+        del src, dst
 
     for _ in range(args.warmup):
         step()
