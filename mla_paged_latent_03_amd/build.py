@@ -4,6 +4,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -19,18 +20,39 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", "-Wa
          "-I" + os.path.join(ROOT, "include")]
 
 
+def _device_asm_cmd(out: str):
+    flags = [f for f in FLAGS if f not in ("-shared", "-Wall")]
+    return [HIPCC] + flags + ["--offload-device-only", "-S", "-o", out, SOURCES[0]]
+
+
 def build(verbose: bool = False) -> str:
+    """Compile the library and, alongside, the kernels' gfx950 assembly; fail
+    if the assembly shows a hazard before an inline-asm memory instruction."""
+    from mla_paged_latent_03_amd import asm_hazards
+
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + ["-o", tmp] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = ("packed-fp32-ops", "unknown target feature")
-    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in noise))
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+    with tempfile.TemporaryDirectory() as td:
+        asm_path = os.path.join(td, "kernels.s")
+        asm_proc = subprocess.Popen(_device_asm_cmd(asm_path), stdout=subprocess.DEVNULL, stderr=subprocess.PIPE,
+                                    text=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        asm_err = asm_proc.communicate()[1]
+        noise = ("packed-fp32-ops", "unknown target feature")
+        err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in noise))
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + err)
+        if asm_proc.returncode != 0:
+            raise RuntimeError("hipcc (device assembly) failed:\n" + asm_err)
+        if err.strip() and verbose:
+            print(err, file=sys.stderr)
+        with open(asm_path) as f:
+            found = asm_hazards.scan(f.read())
+    if found:
+        os.remove(tmp)
+        raise RuntimeError("hazards before inline-asm memory instructions:\n" + "\n".join(found[:20]))
     os.replace(tmp, LIB)
     return LIB
 

@@ -134,8 +134,15 @@ __device__ inline float sum_across_halves(float x) { return x + other_half(x); }
 // Issued from inline asm so the compiler does not treat it as an LDS store
 // (it would otherwise drain every in-flight DMA before each LDS read it
 // cannot prove disjoint); completion is tracked explicitly with vmcnt.
+//
+// The compiler inserts no hazard wait states before an inline-asm memory
+// instruction, so the DMA helpers carry their own: an LDS DMA reading M0
+// needs one after the SALU write of M0 placed just before it.  A vector
+// memory instruction reading an SGPR needs five after a VALU write of that
+// SGPR; buffer_rsrc() provides those once per descriptor.  The build scans
+// the compiled kernels for both cases (asm_hazards.py).
 __device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_byte_addr) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_byte_addr) : "memory");
 }
 
 // 16-byte buffer -> LDS DMA: lane i reads rsrc.base + voff_i + soff and
@@ -144,15 +151,21 @@ __device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
 // tokens of a tile become zero vectors.  Inline asm for the same reason as
 // dma16().
 __device__ inline void dma16_buf(int voff, i32x4_t rsrc, int soff, uint32_t lds_byte_addr) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_byte_addr)
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+               "{m0}"(lds_byte_addr)
                : "memory");
 }
 // Raw buffer descriptor (gfx9 layout): 48-bit base, stride 0, size in bytes.
+// Its words come from v_readfirstlane (VALU writes of SGPRs); the s_nop 4
+// after them gives the five wait states a vector memory read of those SGPRs
+// needs, and as an asm output the descriptor is not re-derived after it.
 __device__ inline i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
-  return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
-                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+  i32x4_t r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+  asm volatile("s_nop 4" : "+s"(r));
+  return r;
 }
 
 // MFMAs whose accumulator must stay in VGPRs.  The output accumulator O
@@ -416,19 +429,18 @@ mla_partial_kernel(const PartialParams p) {
     for (int m = 0; m < 4; m++) a_off[m] = l32 * K::kRowBytes + 16 * ((2 * m) ^ x);
   }
   // PV operand A = V^T via transpose reads; [read r][fb parity].
+  // fp8: read r covers tokens 16 r + (lane's token), so only read 0's
+  // offsets are kept and read r adds the compile-time 16 r rows.
   constexpr int NRD = FP8 ? 4 : 2;
   int v_off[NRD][2];
   {
     const int i = lane & 15, g = lane >> 4, e = g & 1;
     if (FP8) {
       const int sp = i >> 1, q = i & 1, sig = sp >> 2;
-#pragma unroll
-      for (int r = 0; r < NRD; r++) {
-        const int t = 32 * (r >> 1) + 16 * (r & 1) + 8 * sig + 4 * h + (sp & 3);
-        const int base = t * K::kRowBytes + 16 * (e ^ h) + 8 * q;
-        v_off[r][0] = base + 32 * sig;   // even feature block: fb ^ sig = fb + sig
-        v_off[r][1] = base - 32 * sig;   // odd feature block : fb ^ sig = fb - sig
-      }
+      const int t = 8 * sig + 4 * h + (sp & 3);
+      const int base = t * K::kRowBytes + 16 * (e ^ h) + 8 * q;
+      v_off[0][0] = base + 32 * sig;   // even feature block: fb ^ sig = fb + sig
+      v_off[0][1] = base - 32 * sig;   // odd feature block : fb ^ sig = fb - sig
     } else {
       const int sp = i >> 2, q = i & 3, sig = sp >> 1;
 #pragma unroll
@@ -461,8 +473,8 @@ mla_partial_kernel(const PartialParams p) {
       i32x8_t a;
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const i32x2_t d =
-            __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2_t*)(tile + v_off[r][n & 1] + 32 * n));
+        const i32x2_t d = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (LDS_AS i32x2_t*)(tile + v_off[0][n & 1] + 16 * r * K::kRowBytes + 32 * n));
         a[2 * r] = d[0];
         a[2 * r + 1] = d[1];
       }

@@ -173,3 +173,36 @@ def test_sparse_errors(lib):
     assert lib.mla_sparse_decode(*args, FAKE, 0, *tail) == binding.MLA_ERR_INVALID_ARGUMENT    # K = 0
     big = [2, 1, 16, 10, 64, 5, 300, 0.07, FAKE, 0, FAKE, None, 0, 1, None]
     assert lib.mla_sparse_decode(*args, FAKE, 4096, *big) == binding.MLA_ERR_UNSUPPORTED      # 4096 / 1 split
+
+
+# ------------------------------------------------------------------ inline-asm hazard scan
+
+_DMA = "buffer_load_dwordx4 v1, s[8:11], s12 offen lds"
+
+
+def _asm(*lines):
+    return "\n".join("\t" + l for l in lines)
+
+
+def test_asm_hazard_scan_flags_m0_and_sgpr_hazards():
+    """The build-time scan of the compiled kernels: an LDS DMA in inline asm
+    needs 1 wait state after an SALU write of M0 and 5 after a VALU write of
+    an SGPR it reads; the compiler's own memory instructions are not its
+    concern."""
+    from mla_paged_latent_03_amd import asm_hazards as hz
+    clean = _asm("s_mov_b32 m0, s1", ";;#ASMSTART", "s_nop 0", _DMA, ";;#ASMEND")
+    assert hz.scan(clean) == []
+    no_m0_wait = _asm("s_mov_b32 m0, s1", ";;#ASMSTART", _DMA, ";;#ASMEND")
+    assert len(hz.scan(no_m0_wait)) == 1
+    fresh_sgpr = _asm("v_readfirstlane_b32 s9, v0", "s_mov_b32 m0, s1", ";;#ASMSTART", "s_nop 0", _DMA, ";;#ASMEND")
+    assert len(hz.scan(fresh_sgpr)) == 1
+    fresh_soffset = _asm("v_readlane_b32 s12, v254, 3", "s_nop 1", "s_mov_b32 m0, s1", ";;#ASMSTART", "s_nop 0",
+                         _DMA, ";;#ASMEND")
+    assert len(hz.scan(fresh_soffset)) == 1
+    settled = _asm("v_readfirstlane_b32 s9, v0", ";;#ASMSTART", "s_nop 4", ";;#ASMEND", "s_mov_b32 m0, s1",
+                   ";;#ASMSTART", "s_nop 0", _DMA, ";;#ASMEND")
+    assert hz.scan(settled) == []
+    compiler_owned = _asm("v_readfirstlane_b32 s9, v0", "buffer_load_dword v2, v3, s[8:11], 0 offen")
+    assert hz.scan(compiler_owned) == []
+    sparse = _asm("s_add_i32 m0, s37, 0x400", ";;#ASMSTART", "global_load_lds_dwordx4 v[2:3], off", ";;#ASMEND")
+    assert len(hz.scan(sparse)) == 1
