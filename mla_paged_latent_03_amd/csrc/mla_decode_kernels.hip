@@ -574,6 +574,7 @@ mla_partial_kernel(const PartialParams p) {
   constexpr int NEXP = 4;                // exponent stages per token block, four scores each
   struct SmState {
     float ml[K::kTokBlocks];     // this lane's maximum of the block's scores
+    float mr[K::kTokBlocks];     // the row's maximum (feature-split stages)
     float shift[K::kTokBlocks];  // exponent offset applied to the block's scaled scores
     float psum[K::kTokBlocks];   // this lane's sum of the block's unrounded weights
     int sc[K::kTokBlocks];       // fp8: E8M0 scale of the block's weights
@@ -705,6 +706,54 @@ mla_partial_kernel(const PartialParams p) {
     sm_finish(st, pt);
   };
 
+  // Finer stages for the feature-split step, whose schedule gives each one
+  // a matrix product of its own: [mask], max, row (two halves), and eight
+  // exponent stages of two scores each.
+  constexpr int FS_NEXP = 8;
+  constexpr int FS_NSTAGE = 3 + FS_NEXP;
+  auto fs_row_a = [&](int tb, bool& jumped, SmState& st) {
+    const float ml = st.ml[tb] * c_qk;
+    m_seen = fmaxf(m_seen, ml);
+    jumped |= m_ref != kNegBig && ml > m_ref + 64.f;
+    st.mr[tb] = max_across_halves(ml);
+  };
+  auto fs_row_b = [&](int tb, SmState& st) {
+    const float mrow = st.mr[tb];
+    if (m_ref == kNegBig && mrow != -INFINITY) m_ref = ceilf(mrow);
+    const float mi = mrow == -INFINITY ? m_ref : ceilf(mrow);
+    st.shift[tb] = 8.f - mi;
+    const float dexp = fminf(mi - m_ref, 64.f);
+    st.sc[tb] = dexp < -126.f ? 0 : (int)dexp + 127;
+    pin(st.sc[tb]);
+    pin(st.shift[tb]);
+  };
+  // Scores 2d and 2d+1 of token block tb: byte pair d & 1 of P word 4 tb + d / 2.
+  auto fs_exp = [&](f32x16_t (&sacc)[K::kTokBlocks], int tb, int d, SmState& st, PTile& pt) {
+    const float sh = st.shift[tb];
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][2 * d], c_qk, sh));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][2 * d + 1], c_qk, sh));
+    st.psum[tb] = d == 0 ? e0 + e1 : st.psum[tb] + (e0 + e1);
+    pin(st.psum[tb]);
+    // The first pair fills the low half; the high half is written by the
+    // second pair, so the word's earlier contents do not matter.
+    int w;
+    if (d & 1) w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pt.pb[4 * tb + d / 2], true);
+    else w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, __builtin_nondeterministic_value(0), false);
+    pin(w);
+    pt.pb[4 * tb + d / 2] = w;
+  };
+  auto fs_stage = [&](int k, bool mask, f32x16_t (&sacc)[K::kTokBlocks], int i, int tb, bool& jumped,
+                      SmState& st, PTile& pt) {
+    if (mask) {
+      if (k == 0) { sm_mask(sacc, i, tb); return; }
+      k -= 1;
+    }
+    if (k == 0) sm_max(sacc, tb, st);
+    else if (k == 1) fs_row_a(tb, jumped, st);
+    else if (k == 2) fs_row_b(tb, st);
+    else if (k < FS_NSTAGE) fs_exp(sacc, tb, k - 3, st, pt);
+  };
+
   // ---- tiles [0, n_clean) need no mask: every row sees all their tokens
   // (dense: the tile ends at or before the first draft row's causal limit).
   // The tiles after them take the masked softmax.
@@ -810,68 +859,93 @@ mla_partial_kernel(const PartialParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // One step of the pipelined loop with the feature split.  Right after the
-  // barrier the wave runs the PV products of its own row block, whose
-  // operands are already in registers (its own P tile, and this tile's Vᵀ
-  // loaded at the end of the previous step), while the QK operands of tile
-  // i+1 arrive from LDS.  Then QK of tile i+1 (token block 0, then block 1)
-  // with the DMA spread between its products and block 0's softmax between
-  // block 1's products; then the PV of the other row blocks with block 1's
-  // softmax between them.  The new P tile is published after every wave has
-  // read the old one, and the next tile's Vᵀ is loaded for the next step.
-  auto pipe_step_fs = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, i32x8_t (&vt)[4], bool& jumped,
+  // One step of the pipelined loop with the feature split: QK of tile i+1
+  // and PV of tile i in three phases around two barriers.  A tile's softmax
+  // spans two steps, so that its VALU work sits between matrix products in
+  // every phase (one product hides only part of a stage):
+  //  A  QK of tile i+1, token block 0 (9 products), with the last two
+  //     exponent stages of tile i's block 1 and tile i's finish between
+  //     them; then tile i's P tile is published.
+  //  -- barrier: every row block's P tile of tile i is in LDS.
+  //  B  QK of tile i+1, token block 1 (9 products), with the first stages
+  //     of tile i+1's block 0 between them; Vᵀ of tile i is loaded.
+  //  C  PV of tile i: own row block (4 products, P from registers), then
+  //     the other three (12, P from LDS), with the first stages of tile
+  //     i+1's block 1 and the last two of its block 0 between them.
+  // The DMA of tile i+NS-1 is spread over A and B.  Entering, st / pt hold
+  // tile i's softmax state and P tile with all but block 1's last two
+  // exponent stages and the finish done, and sacc[1] holds tile i's block-1
+  // scores; leaving, the same holds for tile i+1.
+  auto pipe_step_fs = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, SmState& st, bool& jumped,
                           auto mask_c) __attribute__((always_inline)) {
-    constexpr bool mask = decltype(mask_c)::value;
+    constexpr bool mask = decltype(mask_c)::value;     // tile i+1's softmax takes the mask
+    constexpr int HEAD = FS_NSTAGE - 4 + (mask ? 1 : 0);   // stages before the last four exponent stages
     constexpr int KS = K::kQkSteps;
+    static_assert(NI == 9 && KS == 9 && NQK == 18, "schedule of the feature-split step");
     wait_vmcnt<NI * (NS - 3)>();
-    wait_lgkm0();      // this wave's P tile of tile i is in LDS, this tile's Vᵀ in registers
-    lds_barrier();     // tile i+1 resident; slot i-1 free; every P tile of tile i published
+    lds_barrier();     // tile i+1 resident; slot i-1 free; every wave done with tile i-1's P tiles
     const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
+    const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
     const int nxt = i + NS - 1;
     const DmaSrc src = dma_prepare(nxt);
-    constexpr int DSTRIDE = NQK / NI;
     opnd_t qa[3];
-    i32x8_t pbq[2];
-    int scq[2];
-    PTile pn;
-    SmState st;
     qa[0] = ld_qk(tq, 0);
     qa[1] = ld_qk(tq, 1);
+    // A: tile i's block-1 exponent stages 4..7 at a = 0, 2, 4, 6, finish at 7,
+    // publish at 8; DMA instructions 0..3 at a = 1, 3, 5, 7.
 #pragma unroll
-    for (int f = 0; f < 4; f++) {
+    for (int a = 0; a < KS; a++) {
+      qa[(a + 2) % 3] = ld_qk(tq, a + 2);
       __builtin_amdgcn_sched_barrier(0);
-      fs_pv_mfma(0, f, vt[f], pt.pb, pt.sc);
+      qk_mfma(sacc, a, qa[a % 3]);
+      if (a % 2 == 0 && a < 8) fs_exp(sacc, 1, 4 + a / 2, st, pt);
+      if (a == 7) sm_finish(st, pt);
+      if (a == 8) fs_write_p(pt);
+      if (a % 2 == 1) dma_issue(src, nxt % NS, a / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
+    wait_lgkm0();
+    lds_barrier();     // every P tile of tile i published
+    // B: tile i+1's block-0 stages 0..HEAD-1 at b = 1..HEAD; Vᵀ of tile i at
+    // b = 0, 2, 4, 6; DMA instructions 4..8 at b = 0, 2, 4, 6, 8.
+    SmState sn;
+    PTile pn;
+    i32x8_t vt[4];
 #pragma unroll
-    for (int n = 0; n < NQK; n++) {
+    for (int b = 0; b < KS; b++) {
+      const int n = KS + b;
       if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(tq, n + 2);
-      if (n == NQK - 1) fs_read_p((wave + 1) & 3, pbq[0], scq[0]);
+      if (b % 2 == 0 && b < 8) vt[b / 2] = fs_ld_v(tv, b / 2);
       __builtin_amdgcn_sched_barrier(0);
       qk_mfma(sacc, n, qa[n % 3]);
-      if (n == KS) mfma_drain(sacc[0]);          // block 0's chain ended one product ago
-      if (n > KS) sm_block_stage(n - KS - 1, mask, sacc, i + 1, 0, jumped, st, pn);
-      if (n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
+      if (b == 0) mfma_drain(sacc[0]);           // block 0's chain ended one product ago
+      if (b >= 1 && b - 1 < HEAD) fs_stage(b - 1, mask, sacc, i + 1, 0, jumped, sn, pn);
+      if (b % 2 == 0) dma_issue(src, nxt % NS, 4 + b / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
+    static_assert(FS_NSTAGE - 4 + 1 <= KS - 1, "block 0's first stages fit phase B");
+    // C: PV of tile i (own row block at m = 0..3, the others at m = 4..15);
+    // tile i+1's block-1 stages 0..HEAD-1 at odd m, block-0 exponent stages
+    // 4..7 at m = 2, 6, 10, 14.
+    i32x8_t pbq[2];
+    int scq[2];
 #pragma unroll
-    for (int n = 0; n < 12; n++) {
-      const int j = n >> 2, f = n & 3;
-      if (f == 0 && j + 1 < 3) fs_read_p((wave + 2 + j) & 3, pbq[(j + 1) & 1], scq[(j + 1) & 1]);
+    for (int m = 0; m < 16; m++) {
+      const int n = m - 4, j = n >> 2, f = n & 3;
+      if (m == 2) fs_read_p((wave + 1) & 3, pbq[0], scq[0]);
+      if (m >= 4 && f == 0 && j + 1 < 3) fs_read_p((wave + 2 + j) & 3, pbq[(j + 1) & 1], scq[(j + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      fs_pv_mfma(1 + j, f, vt[f], pbq[j & 1], scq[j & 1]);
-      if (n == 0) mfma_drain(sacc[1]);
-      if (n > 0) sm_block_stage(n - 1, mask, sacc, i + 1, 1, jumped, st, pn);
-      if (n == NSTAGE_BLOCK + 2) sm_finish(st, pn);
+      if (m < 4) fs_pv_mfma(0, m, vt[m], pt.pb, pt.sc);
+      else fs_pv_mfma(1 + j, f, vt[f], pbq[j & 1], scq[j & 1]);
+      if (m == 0) mfma_drain(sacc[1]);           // block 1's chain ended one product ago
+      if (m % 2 == 1 && m / 2 < HEAD) fs_stage(m / 2, mask, sacc, i + 1, 1, jumped, sn, pn);
+      if (m % 4 == 2) fs_exp(sacc, 0, 4 + m / 4, sn, pn);
       __builtin_amdgcn_sched_barrier(0);
     }
-    static_assert(NSTAGE_BLOCK + 3 <= 12, "block 1's stages fit between the other row blocks' products");
+    static_assert(FS_NSTAGE - 4 + 1 <= 8, "block 1's first stages fit phase C");
     row_sum_mfma(pt);
-    lds_barrier();     // every wave has read the P tiles of tile i
-#pragma unroll
-    for (int f = 0; f < 4; f++) vt[f] = fs_ld_v(tq, f);   // Vᵀ of tile i+1 for the next step
-    fs_write_p(pn);
     pt = pn;
+    st = sn;
   };
 
   // bf16 form of the step: its query operand takes 144 VGPRs, which leaves
@@ -945,28 +1019,42 @@ mla_partial_kernel(const PartialParams p) {
           drain_scores(sacc);
         }
         PTile pt;
-        softmax_all(sacc, 0, jumped, pt);
-
         int i = 0;
-        i32x8_t vt[4];   // FS: Vᵀ operands of the tile whose PV comes next (own features)
         if constexpr (FS) {
-          fs_write_p(pt);
+          // Tile 0's softmax up to the hand-over point of the step (block 1's
+          // last two exponent stages and the finish come in step 0).
+          SmState st;
 #pragma unroll
-          for (int f = 0; f < 4; f++) vt[f] = fs_ld_v(lds, f);
-          for (; i + 1 < n_clean; i++) pipe_step_fs(i, sacc, pt, vt, jumped, std::false_type{});
-          for (; i + 1 < n_tiles; i++) pipe_step_fs(i, sacc, pt, vt, jumped, std::true_type{});
-        } else if constexpr (FP8) {
-          for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, std::false_type{});
-          for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, std::true_type{});
+          for (int tb = 0; tb < K::kTokBlocks; tb++)
+#pragma unroll
+            for (int k = 0; k < FS_NSTAGE + 1 - (tb == 1 ? 4 : 0); k++)
+              fs_stage(k, true, sacc, 0, tb, jumped, st, pt);
+          for (; i + 1 < n_clean; i++) pipe_step_fs(i, sacc, pt, st, jumped, std::false_type{});
+          for (; i + 1 < n_tiles; i++) pipe_step_fs(i, sacc, pt, st, jumped, std::true_type{});
+          // Last tile: the rest of its softmax, publish, PV.
+#pragma unroll
+          for (int d = 4; d < FS_NEXP; d++) fs_exp(sacc, 1, d, st, pt);
+          sm_finish(st, pt);
+          fs_write_p(pt);
         } else {
-          for (; i + 1 < n_clean; i++) pipe_step_qv(i, sacc, pt, jumped, std::false_type{});
-          for (; i + 1 < n_tiles; i++) pipe_step_qv(i, sacc, pt, jumped, std::true_type{});
+          softmax_all(sacc, 0, jumped, pt);
+          if constexpr (FP8) {
+            for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, std::false_type{});
+            for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, std::true_type{});
+          } else {
+            for (; i + 1 < n_clean; i++) pipe_step_qv(i, sacc, pt, jumped, std::false_type{});
+            for (; i + 1 < n_tiles; i++) pipe_step_qv(i, sacc, pt, jumped, std::true_type{});
+          }
         }
 
         // Last tile: PV only.
         if constexpr (FS) {
           wait_lgkm0();
           lds_barrier();   // every P tile of the last tile published
+          const LDS_AS uint8_t* tv = lds + ((n_tiles - 1) % NS) * kTileBytes;
+          i32x8_t vt[4];
+#pragma unroll
+          for (int f = 0; f < 4; f++) vt[f] = fs_ld_v(tv, f);
           fs_pv_tile(vt, pt);
           row_sum_mfma(pt);
         } else {
