@@ -500,7 +500,10 @@ mla_partial_kernel(const PartialParams p) {
   // maximum ever exceeds m_ref by more than 2^64 (fp32 headroom for O) is the
   // whole unit run a second time with m_ref = that row's true maximum.
   f32x16_t oacc[16];
-  f32x16_t lsum;                   // ones x P^T: row sum of the rounded weights (normalizes out)
+  // fp8: ones x P^T, the row sum of the rounded weights, normalizes O, so
+  // that the up to 2^-4 rounding of each weight cancels.  bf16 weights are
+  // rounded to 2^-9, and O is normalized by the exact fp32 sum l_f instead.
+  f32x16_t lsum;
   float m_ref = kNegBig;
   float m_seen = -INFINITY;        // running lane maximum, for the second pass
   float l_f = 0.f;                 // this half's sum of the unrounded weights (gives lse)
@@ -549,10 +552,8 @@ mla_partial_kernel(const PartialParams p) {
     if constexpr (FP8) {
       mfma_f8_acc(lsum, ones8, pt.pb, e8m0_one, pt.sc);
       if constexpr (RESID) mfma_f8_acc(lsum, ones8, pt.pbl, e8m0_one, pt.scl);
-    } else {
-      mfma_bf16_acc(lsum, ones16, __builtin_bit_cast(bf16x8_t, i32x4_t{pt.pb[0], pt.pb[1], pt.pb[2], pt.pb[3]}));
-      mfma_bf16_acc(lsum, ones16, __builtin_bit_cast(bf16x8_t, i32x4_t{pt.pb[4], pt.pb[5], pt.pb[6], pt.pb[7]}));
     }
+    (void)ones16;
   };
 
   // Padding after a tile's QK chain, tied to its score accumulators.
@@ -963,16 +964,22 @@ mla_partial_kernel(const PartialParams p) {
     const DmaSrc src = dma_prepare(nxt);
     constexpr int DSTRIDE = NQK / NI;
     static_assert(NQK % NI == 0, "DMA spread");
-    opnd_t qa[2], va[2];
-    qa[0] = ld_qk(tq, 0);
-    va[0] = ld_pv(tv, 0);
+    // Operands are loaded QD products ahead: one QK and one PV product take
+    // about 64 cycles, less than an LDS read's latency under load.
+    constexpr int QD = 2;
+    opnd_t qa[QD + 1], va[QD + 1];
+#pragma unroll
+    for (int n = 0; n < QD; n++) {
+      qa[n] = ld_qk(tq, n);
+      va[n] = ld_pv(tv, n);
+    }
 #pragma unroll
     for (int n = 0; n < (NQK > NPV ? NQK : NPV); n++) {
-      if (n + 1 < NQK) qa[(n + 1) & 1] = ld_qk(tq, n + 1);
-      if (n + 1 < NPV) va[(n + 1) & 1] = ld_pv(tv, n + 1);
+      if (n + QD < NQK) qa[(n + QD) % (QD + 1)] = ld_qk(tq, n + QD);
+      if (n + QD < NPV) va[(n + QD) % (QD + 1)] = ld_pv(tv, n + QD);
       __builtin_amdgcn_sched_barrier(0);
-      if (n < NQK) qk_mfma(sacc, n, qa[n & 1]);
-      if (n < NPV) pv_mfma(n, va[n & 1], pt);
+      if (n < NQK) qk_mfma(sacc, n, qa[n % (QD + 1)]);
+      if (n < NPV) pv_mfma(n, va[n % (QD + 1)], pt);
       if (n < NQK && n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1121,7 +1128,7 @@ mla_partial_kernel(const PartialParams p) {
       }
       wait_vmcnt<0>();   // the zero fill past the end must land before the LDS is reused
     }
-    mfma_drain(lsum);
+    if constexpr (FP8) mfma_drain(lsum);
 
     // ---- second pass needed?  (workgroup-uniform: all waves share the DMA)
     if (pass == 1) break;
@@ -1138,7 +1145,7 @@ mla_partial_kernel(const PartialParams p) {
   // ---- epilogue: normalize, write final output or the split partial
   const float off = FP8 ? 8.f : 0.f;
   l_f = sum_across_halves(l_f);
-  const float l_q = lsum[0];       // every element of a lane's lsum holds its row's sum
+  const float l_q = FP8 ? lsum[0] : l_f;   // fp8: every element of a lane's lsum holds its row's sum
   const bool empty = !(l_f > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_q;
   const float lse_v = empty ? -INFINITY : (m_ref - off + __builtin_amdgcn_logf(l_f)) * kLn2;

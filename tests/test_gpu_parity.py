@@ -98,13 +98,21 @@ def test_empty_sequence_gives_zero_and_neg_inf():
         check_full(inp, s, "empty seq")
 
 
-def test_single_token_closed_form_is_exact():
-    inp = wl.make_inputs(2, 32, 1, [1, 1], kv_dtype="bf16", out_dtype="f32", seed=5)
-    out, lse = run_case(inp, 1, "single token")
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_single_token_closed_form_is_exact(out_dtype):
+    """kv_len 1: out = c_0 and lse = s_0.  The weight is 1; bf16 output is
+    bit-exact.  O is normalized by the fp32 sum of the unrounded weight, a
+    few fp32 ulps away from 1, so f32 output matches to 1e-6 relative."""
+    inp = wl.make_inputs(2, 32, 1, [1, 1], kv_dtype="bf16", out_dtype=out_dtype, seed=5)
+    out, lse = run_case(inp, 1, "single token %s" % out_dtype)
     kv = inp.kv_cache.to(torch.float32)
     for b in range(2):
         c0 = kv[int(inp.block_table[b, 0]), 0, :512]
-        assert torch.equal(out[b, 0].cpu(), c0.expand(32, 512)), "out must be the token's latent exactly"
+        got = out[b, 0].cpu().float()
+        if out_dtype == "bf16":
+            assert torch.equal(got, c0.expand(32, 512)), "out must be the token's latent exactly"
+        else:
+            assert torch.allclose(got, c0.expand(32, 512), rtol=1e-6, atol=0)
         s0 = inp.softmax_scale * (inp.q_nope[b, 0].double() @ kv[int(inp.block_table[b, 0]), 0, :512].double() +
                                   inp.q_pe[b, 0].double() @ kv[int(inp.block_table[b, 0]), 0, 512:].double())
         assert torch.allclose(lse[b, 0].cpu().double(), s0, rtol=1e-5, atol=1e-5)
