@@ -322,36 +322,9 @@ mla_partial_kernel(const PartialParams p) {
   }
   __syncthreads();
 
-  // ---- query operand in registers (B side: lane holds row l32, a K slice)
-  // bf16: step k covers features 16k .. 16k+15; lane half h holds 8 of them.
-  // fp8 : step k covers features 64k .. 64k+63; lane half h holds 32 of them.
+  // ---- query operand registers (filled after the first DMAs are issued)
   constexpr int QREGS = FP8 ? 8 * K::kQkSteps : 4 * K::kQkSteps;
   int qreg[QREGS];
-  {
-    // Rows past the end read row 0 of the sequence (always present) and are zeroed.
-    const int64_t qsafe = row_ok ? qrow : (int64_t)b * p.R;
-    const uint8_t* qn = p.q_nope + qsafe * (512 * (FP8 ? 1 : 2));
-    const uint8_t* qp = p.q_pe + qsafe * (64 * (FP8 ? 1 : 2));
-    const int keep = row_ok ? -1 : 0;
-    if (FP8) {
-#pragma unroll
-      for (int k = 0; k < K::kQkSteps; k++) {
-        const uint8_t* src = k < 8 ? qn + 64 * k + 32 * h : qp + 32 * h;
-        const i32x4_t a = *(const i32x4_t*)src;
-        const i32x4_t c = *(const i32x4_t*)(src + 16);
-#pragma unroll
-        for (int i = 0; i < 4; i++) { qreg[8 * k + i] = a[i] & keep; qreg[8 * k + 4 + i] = c[i] & keep; }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < K::kQkSteps; k++) {
-        const uint8_t* src = k < 32 ? qn + 2 * (16 * k + 8 * h) : qp + 2 * (16 * (k - 32) + 8 * h);
-        const i32x4_t a = *(const i32x4_t*)src;
-#pragma unroll
-        for (int i = 0; i < 4; i++) qreg[4 * k + i] = a[i] & keep;
-      }
-    }
-  }
 
   // ---- DMA source offsets.  Wave w fills tile units [w*NI*64, (w+1)*NI*64):
   // instruction j writes LDS units pos = (w*NI + j)*64 + lane, i.e. token
@@ -377,7 +350,7 @@ mla_partial_kernel(const PartialParams p) {
     LDS_AS const int* rows;
     int n_valid;
   };
-  auto dma_prepare = [&](int i) -> DmaSrc {
+  auto dma_prepare = [&](int i) __attribute__((always_inline)) -> DmaSrc {
     DmaSrc d;
     const bool real = i < n_tiles;
     if (SPARSE) {
@@ -396,7 +369,7 @@ mla_partial_kernel(const PartialParams p) {
     return d;
   };
   // DMA instruction j of a tile into ring slot `slot`.
-  auto dma_issue = [&](const DmaSrc& d, int slot, int j) {
+  auto dma_issue = [&](const DmaSrc& d, int slot, int j) __attribute__((always_inline)) {
     const uint32_t dst = lds_u32 + slot * kTileBytes + (wave * NI + j) * 1024;
     if (SPARSE) {
       const int tc = dma_tc[j % NPRE];
@@ -410,11 +383,54 @@ mla_partial_kernel(const PartialParams p) {
       dma16_buf(dma_tc[j % NPRE], d.rsrc, (j / NPRE) * 16 * K::kRowBytes, dst);
     }
   };
-  auto issue_tile = [&](int i, int slot) {
+  auto issue_tile = [&](int i, int slot) __attribute__((always_inline)) {
     const DmaSrc d = dma_prepare(i);
 #pragma unroll
     for (int j = 0; j < NI; j++) dma_issue(d, slot, j);
   };
+
+  // Pass 0's first tiles go out before the query loads, so that the two
+  // latencies overlap.  (A second pass issues them again at its start.)
+  auto issue_first_tiles = [&]() __attribute__((always_inline)) {
+    if (n_tiles > 0) {
+      if constexpr (PIPE) {
+#pragma unroll
+        for (int i = 0; i < NS - 1; i++) issue_tile(i, i);
+      } else {
+        issue_tile(0, 0);
+      }
+    }
+  };
+  issue_first_tiles();
+
+  // ---- query operand in registers (B side: lane holds row l32, a K slice)
+  // bf16: step k covers features 16k .. 16k+15; lane half h holds 8 of them.
+  // fp8 : step k covers features 64k .. 64k+63; lane half h holds 32 of them.
+  {
+    // Rows past the end read row 0 of the sequence (always present) and are zeroed.
+    const int64_t qsafe = row_ok ? qrow : (int64_t)b * p.R;
+    const uint8_t* qn = p.q_nope + qsafe * (512 * (FP8 ? 1 : 2));
+    const uint8_t* qp = p.q_pe + qsafe * (64 * (FP8 ? 1 : 2));
+    const int keep = row_ok ? -1 : 0;
+    if (FP8) {
+#pragma unroll
+      for (int k = 0; k < K::kQkSteps; k++) {
+        const uint8_t* src = k < 8 ? qn + 64 * k + 32 * h : qp + 32 * h;
+        const i32x4_t a = *(const i32x4_t*)src;
+        const i32x4_t c = *(const i32x4_t*)(src + 16);
+#pragma unroll
+        for (int i = 0; i < 4; i++) { qreg[8 * k + i] = a[i] & keep; qreg[8 * k + 4 + i] = c[i] & keep; }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < K::kQkSteps; k++) {
+        const uint8_t* src = k < 32 ? qn + 2 * (16 * k + 8 * h) : qp + 2 * (16 * (k - 32) + 8 * h);
+        const i32x4_t a = *(const i32x4_t*)src;
+#pragma unroll
+        for (int i = 0; i < 4; i++) qreg[4 * k + i] = a[i] & keep;
+      }
+    }
+  }
 
   // ---- per-lane LDS read offsets (within a tile)
   // QK operand A = K tile rows: token 32*tb + l32, unit(s) for step k.
@@ -1007,8 +1023,7 @@ mla_partial_kernel(const PartialParams p) {
       if (n_tiles > 0) {
         // Prologue: NS-1 tiles in flight (zero fills past the end keep the
         // count uniform), then QK and softmax of tile 0.
-#pragma unroll
-        for (int i = 0; i < NS - 1; i++) issue_tile(i, i);
+        if (pass > 0) issue_first_tiles();
         wait_vmcnt<NI * (NS - 2)>();
         lds_barrier();
         f32x16_t sacc[K::kTokBlocks];
@@ -1088,7 +1103,7 @@ mla_partial_kernel(const PartialParams p) {
       // flight at a time).  Past the end the slot gets a zero fill, which
       // keeps the wait a constant.
       static_assert(NS == 2, "two-slot loop");
-      if (n_tiles > 0) issue_tile(0, 0);
+      if (pass > 0) issue_first_tiles();
       for (int i = 0; i < n_tiles; i++) {
         wait_vmcnt<0>();
         if (RG > 1) lds_barrier();   // tile i complete; every wave is done with tile i-1's slot
