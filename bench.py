@@ -120,8 +120,11 @@ def load_traffic(workload: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # The clock settles about 15 ms into a burst of calls (a short fast phase
+    # on a cool GPU, then a dip, then the sustained rate), so the default
+    # warm-up covers that before timing the steady state.
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -232,14 +232,19 @@ mla_partial_kernel(const PartialParams p) {
   static_assert(!PIPE || NS >= 3, "the pipelined loop keeps two tiles resident");
   static_assert(!FS || (FP8 && !SPARSE && RG == 4 && !RESID), "feature split: dense fp8, four waves");
   constexpr int kTableCap = SPARSE ? kSparseChunkMax : kDensePagesMax;
+  // Dense: int32 page per page of the unit.  Sparse: the 64-bit address of
+  // each index's token row (the zero row for a skipped entry), then one
+  // tile's worth of zero-row addresses that tiles past the end read.
+  constexpr int kTableBytes = SPARSE ? (kTableCap + K::kTileTok) * 8 : kTableCap * 4;
   constexpr int kPBytes = FS ? 4 * 2048 : 0;      // FS: P tile of each row block (64 lanes x 32 B)
   constexpr int kScBytes = FS ? 4 * 64 * 4 : 0;   // FS: E8M0 scales of each row block (per lane)
 
   // LDS: [ring of NS tiles][unit table: int32 x kTableCap][FS: P tiles][FS: scales][redo flag]
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kTileBytes + kTableCap * 4 + kPBytes + kScBytes + 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kTileBytes + kTableBytes + kPBytes + kScBytes + 16];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
   LDS_AS int* table = (LDS_AS int*)(lds + NS * kTileBytes);
-  LDS_AS uint8_t* pbuf = lds + NS * kTileBytes + kTableCap * 4;
+  LDS_AS uint64_t* table64 = (LDS_AS uint64_t*)(lds + NS * kTileBytes);
+  LDS_AS uint8_t* pbuf = lds + NS * kTileBytes + kTableBytes;
   LDS_AS int* scbuf = (LDS_AS int*)(pbuf + kPBytes);
   LDS_AS int* redo_flag = (LDS_AS int*)(pbuf + kPBytes + kScBytes);
 
@@ -297,22 +302,24 @@ mla_partial_kernel(const PartialParams p) {
   const int n_vis = L - p.T + t_row + 1;  // dense: visible tokens of this row
 
   // ---- unit table in LDS.  Dense: physical page of each page of the unit
-  // (-1 if out of range).  Sparse: physical token row of each index (-1 for
-  // padding / out-of-range entries).
+  // (-1 if out of range).  Sparse: address of each index's token row, or of
+  // the zero row for padding / out-of-range entries.
+  const uint64_t zero_row = (uint64_t)(uintptr_t)g_zero_row;
   if (SPARSE) {
     const int32_t* idx = p.topk + ((int64_t)b * p.T + (rb / p.n_hb)) * p.K + idx_begin;
     const int n_ent = n_tiles * K::kTileTok;
     for (int e = threadIdx.x; e < n_ent; e += 64 * RG) {
-      int phys = -1;
+      uint64_t a = zero_row;
       if (e < idx_count) {
         const int j = idx[e];
         if (j >= 0 && j < L) {
           const int pg = p.block_table[(int64_t)b * p.MB + (j >> 6)];
-          if (pg >= 0 && pg < p.NB) phys = pg * 64 + (j & 63);
+          if (pg >= 0 && pg < p.NB) a = (uint64_t)(uintptr_t)(p.kv + ((int64_t)pg * 64 + (j & 63)) * K::kRowBytes);
         }
       }
-      table[e] = phys;
+      table64[e] = a;
     }
+    if (threadIdx.x < K::kTileTok) table64[kTableCap + threadIdx.x] = zero_row;
   } else {
     const int32_t* bt = p.block_table + (int64_t)b * p.MB + page0;
     for (int e = threadIdx.x; e < n_unit_pages; e += 64 * RG) {
@@ -347,7 +354,7 @@ mla_partial_kernel(const PartialParams p) {
   // the tile's slice of the row table (n_valid = 0 for a tile past the end).
   struct DmaSrc {
     i32x4_t rsrc;
-    LDS_AS const int* rows;
+    LDS_AS const uint64_t* rows;   // sparse: the tile's token-row addresses
     int n_valid;
   };
   auto dma_prepare = [&](int i) __attribute__((always_inline)) -> DmaSrc {
@@ -355,7 +362,7 @@ mla_partial_kernel(const PartialParams p) {
     const bool real = i < n_tiles;
     if (SPARSE) {
       d.rsrc = i32x4_t{0, 0, 0, 0};
-      d.rows = table + (real ? i : 0) * K::kTileTok;
+      d.rows = table64 + (real ? i * K::kTileTok : kTableCap);   // past the end: zero rows
       d.n_valid = real ? K::kTileTok : 0;
     } else {
       const int tok0 = tok_begin + (real ? i : 0) * K::kTileTok;
@@ -363,7 +370,7 @@ mla_partial_kernel(const PartialParams p) {
       const int n_valid = (real && pg >= 0) ? min(K::kTileTok, L - tok0) : 0;
       d.rsrc = buffer_rsrc(p.kv + ((int64_t)(pg >= 0 ? pg : 0) * 64 + (tok0 & 63)) * K::kRowBytes,
                            (uint32_t)(n_valid * K::kRowBytes));
-      d.rows = table;
+      d.rows = table64;
       d.n_valid = n_valid;
     }
     return d;
@@ -375,10 +382,7 @@ mla_partial_kernel(const PartialParams p) {
       const int tc = dma_tc[j % NPRE];
       const int t = (tc & 255) + (j / NPRE) * 16;
       const int cb = tc >> 8;
-      const int phys = d.rows[t];
-      const uint8_t* src =
-          (t < d.n_valid && phys >= 0) ? p.kv + (int64_t)phys * K::kRowBytes + cb : g_zero_row;
-      dma16(src, dst);
+      dma16((const void*)(uintptr_t)(d.rows[t] + cb), dst);
     } else {
       dma16_buf(dma_tc[j % NPRE], d.rsrc, (j / NPRE) * 16 * K::kRowBytes, dst);
     }
@@ -602,8 +606,8 @@ mla_partial_kernel(const PartialParams p) {
   // branches: a branch here splits the loop body and costs registers.
   auto sm_mask = [&](f32x16_t (&sacc)[K::kTokBlocks], int i, int tb) {
     if (SPARSE) {
-      const int phys = lane < K::kTileTok ? table[i * K::kTileTok + lane] : 0;
-      const uint64_t valid = __builtin_amdgcn_ballot_w64(phys >= 0) | (K::kTileTok == 64 ? 0ull : ~0ull << 32);
+      const uint64_t a = lane < K::kTileTok ? table64[i * K::kTileTok + lane] : zero_row;
+      const uint64_t valid = __builtin_amdgcn_ballot_w64(a != zero_row) | (K::kTileTok == 64 ? 0ull : ~0ull << 32);
       const uint64_t mine = valid >> (4 * h);
 #pragma unroll
       for (int v = 0; v < 16; v++)
@@ -1251,13 +1255,28 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(const MergeParams p) {
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) zs += __shfl_xor(zs, d);
       z += zs;
+      // Eight splits at a time: all of a group's loads are issued before any
+      // is used, so their latencies overlap.  (Rows of 513 floats are only
+      // 4-byte aligned, hence single-float loads.)
       const int ns = min(64, p.S - s0);
-      for (int k = 0; k < ns; k++) {
-        const float wk = __shfl(w, k);
-        if (wk == 0.f) continue;
-        const float* src = base + (int64_t)(s0 + k) * kPartialWidth + 8 * lane;
+      for (int k0 = 0; k0 < ns; k0 += 8) {
+        float v[8][8];
 #pragma unroll
-        for (int c = 0; c < 8; c++) acc[c] += wk * src[c];
+        for (int k = 0; k < 8; k++) {
+          if (k0 + k < ns) {
+            const float* src = base + (int64_t)(s0 + k0 + k) * kPartialWidth + 8 * lane;
+#pragma unroll
+            for (int c = 0; c < 8; c++) v[k][c] = src[c];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          if (k0 + k < ns) {
+            const float wk = __shfl(w, k0 + k);
+#pragma unroll
+            for (int c = 0; c < 8; c++) acc[c] += wk * v[k][c];
+          }
+        }
       }
     }
     const float inv = 1.f / z;
