@@ -969,13 +969,14 @@ mla_partial_kernel(const PartialParams p) {
     st = sn;
   };
 
-  // bf16 form of the step: its query operand takes 144 VGPRs, which leaves
-  // no room to keep scores live across the PV products.  QK of tile i+1 and
-  // PV of tile i alternate product by product instead, and the (short)
-  // softmax follows them.
-  auto pipe_step_qv = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped,
-                          auto mask_c) __attribute__((always_inline)) {
+  // bf16 step: the QK chain of tile i+1 (one token block of 32, 36 products)
+  // with the DMA of tile i+NS-1 spread between its products, then the 32 PV
+  // products of tile i with the softmax stages of tile i+1 between them.
+  // Operands are loaded QD products ahead.
+  auto pipe_step_bf16 = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped,
+                            auto mask_c) __attribute__((always_inline)) {
     constexpr bool mask = decltype(mask_c)::value;
+    constexpr int QD = 2;
     wait_vmcnt<NI * (NS - 3)>();
     lds_barrier();
     const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
@@ -984,32 +985,36 @@ mla_partial_kernel(const PartialParams p) {
     const DmaSrc src = dma_prepare(nxt);
     constexpr int DSTRIDE = NQK / NI;
     static_assert(NQK % NI == 0, "DMA spread");
-    // Operands are loaded QD products ahead: one QK and one PV product take
-    // about 64 cycles, less than an LDS read's latency under load.
-    constexpr int QD = 2;
     opnd_t qa[QD + 1], va[QD + 1];
 #pragma unroll
-    for (int n = 0; n < QD; n++) {
-      qa[n] = ld_qk(tq, n);
-      va[n] = ld_pv(tv, n);
-    }
+    for (int n = 0; n < QD; n++) qa[n] = ld_qk(tq, n);
 #pragma unroll
-    for (int n = 0; n < (NQK > NPV ? NQK : NPV); n++) {
+    for (int n = 0; n < NQK; n++) {
       if (n + QD < NQK) qa[(n + QD) % (QD + 1)] = ld_qk(tq, n + QD);
+      if (n + QD >= NQK) va[n + QD - NQK] = ld_pv(tv, n + QD - NQK);
+      __builtin_amdgcn_sched_barrier(0);
+      qk_mfma(sacc, n, qa[n % (QD + 1)]);
+      if (n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    PTile pn;
+    SmState st;
+    constexpr int NSB = NSTAGE_BLOCK + (mask ? 1 : 0);
+#pragma unroll
+    for (int n = 0; n < NPV; n++) {
       if (n + QD < NPV) va[(n + QD) % (QD + 1)] = ld_pv(tv, n + QD);
       __builtin_amdgcn_sched_barrier(0);
-      if (n < NQK) qk_mfma(sacc, n, qa[n % (QD + 1)]);
-      if (n < NPV) pv_mfma(n, va[n % (QD + 1)], pt);
-      if (n < NQK && n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
+      pv_mfma(n, va[n % (QD + 1)], pt);
+      if (n == 0) mfma_drain(sacc[0]);           // the QK chain ended one product ago
+      // stages at every third product from n = 1, then the finish
+      if (n >= 1 && (n - 1) % 3 == 0 && (n - 1) / 3 < NSB) sm_block_stage((n - 1) / 3, mask, sacc, i + 1, 0, jumped, st, pn);
+      if (n == 3 * NSB + 1) sm_finish(st, pn);
       __builtin_amdgcn_sched_barrier(0);
     }
-    row_sum_mfma(pt);
-    drain_scores(sacc);
-    SmState st;
-#pragma unroll
-    for (int k = 0; k < NSTAGE_BLOCK + 1; k++) sm_block_stage(k, mask, sacc, i + 1, 0, jumped, st, pt);
-    sm_finish(st, pt);
+    static_assert(3 * (NSTAGE_BLOCK + 1) + 1 < NPV, "the bf16 softmax stages fit between the PV products");
+    pt = pn;
   };
+
 
   // ---- the tile loop, at most twice (second pass: exact reference)
   for (int pass = 0; pass < 2; pass++) {
@@ -1068,8 +1073,8 @@ mla_partial_kernel(const PartialParams p) {
             for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, std::false_type{});
             for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, std::true_type{});
           } else {
-            for (; i + 1 < n_clean; i++) pipe_step_qv(i, sacc, pt, jumped, std::false_type{});
-            for (; i + 1 < n_tiles; i++) pipe_step_qv(i, sacc, pt, jumped, std::true_type{});
+            for (; i + 1 < n_clean; i++) pipe_step_bf16(i, sacc, pt, jumped, std::false_type{});
+            for (; i + 1 < n_tiles; i++) pipe_step_bf16(i, sacc, pt, jumped, std::true_type{});
           }
         }
 
