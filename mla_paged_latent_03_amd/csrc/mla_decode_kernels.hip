@@ -732,16 +732,19 @@ mla_partial_kernel(const PartialParams p) {
   // exponent stages of two scores each.
   constexpr int FS_NEXP = 8;
   constexpr int FS_NSTAGE = 3 + FS_NEXP;
-  auto fs_row_a = [&](int tb, bool& jumped, SmState& st) {
+  // Unmasked stages (`clean`) run only on tiles after tile 0, which every
+  // row sees in full, so m_ref is set and the scores are finite: the
+  // sentinel and -inf cases drop out.
+  auto fs_row_a = [&](int tb, bool& jumped, SmState& st, bool clean) {
     const float ml = st.ml[tb] * c_qk;
     m_seen = fmaxf(m_seen, ml);
-    jumped |= m_ref != kNegBig && ml > m_ref + 64.f;
+    jumped |= (clean || m_ref != kNegBig) && ml > m_ref + 64.f;
     st.mr[tb] = max_across_halves(ml);
   };
-  auto fs_row_b = [&](int tb, SmState& st) {
+  auto fs_row_b = [&](int tb, SmState& st, bool clean) {
     const float mrow = st.mr[tb];
-    if (m_ref == kNegBig && mrow != -INFINITY) m_ref = ceilf(mrow);
-    const float mi = mrow == -INFINITY ? m_ref : ceilf(mrow);
+    if (!clean && m_ref == kNegBig && mrow != -INFINITY) m_ref = ceilf(mrow);
+    const float mi = (clean || mrow != -INFINITY) ? ceilf(mrow) : m_ref;
     st.shift[tb] = 8.f - mi;
     const float dexp = fminf(mi - m_ref, 64.f);
     st.sc[tb] = dexp < -126.f ? 0 : (int)dexp + 127;
@@ -756,10 +759,11 @@ mla_partial_kernel(const PartialParams p) {
     st.psum[tb] = d == 0 ? e0 + e1 : st.psum[tb] + (e0 + e1);
     pin(st.psum[tb]);
     // The first pair fills the low half; the high half is written by the
-    // second pair, so the word's earlier contents do not matter.
+    // second pair, so the word's earlier contents do not matter: the spent
+    // bits of e0 serve, which spares a register clear.
     int w;
     if (d & 1) w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, pt.pb[4 * tb + d / 2], true);
-    else w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, __builtin_nondeterministic_value(0), false);
+    else w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, __builtin_bit_cast(int, e0), false);
     pin(w);
     pt.pb[4 * tb + d / 2] = w;
   };
@@ -770,8 +774,8 @@ mla_partial_kernel(const PartialParams p) {
       k -= 1;
     }
     if (k == 0) sm_max(sacc, tb, st);
-    else if (k == 1) fs_row_a(tb, jumped, st);
-    else if (k == 2) fs_row_b(tb, st);
+    else if (k == 1) fs_row_a(tb, jumped, st, !mask);
+    else if (k == 2) fs_row_b(tb, st, !mask);
     else if (k < FS_NSTAGE) fs_exp(sacc, tb, k - 3, st, pt);
   };
 
@@ -884,7 +888,7 @@ mla_partial_kernel(const PartialParams p) {
   // and PV of tile i in three phases around two barriers.  A tile's softmax
   // spans two steps, so that its VALU work sits between matrix products in
   // every phase (one product hides only part of a stage):
-  //  A  QK of tile i+1, token block 0 (9 products), with the last two
+  //  A  QK of tile i+1, token block 0 (9 products), with the last four
   //     exponent stages of tile i's block 1 and tile i's finish between
   //     them; then tile i's P tile is published.
   //  -- barrier: every row block's P tile of tile i is in LDS.
@@ -892,9 +896,9 @@ mla_partial_kernel(const PartialParams p) {
   //     of tile i+1's block 0 between them; Vᵀ of tile i is loaded.
   //  C  PV of tile i: own row block (4 products, P from registers), then
   //     the other three (12, P from LDS), with the first stages of tile
-  //     i+1's block 1 and the last two of its block 0 between them.
+  //     i+1's block 1 and the last four of its block 0 between them.
   // The DMA of tile i+NS-1 is spread over A and B.  Entering, st / pt hold
-  // tile i's softmax state and P tile with all but block 1's last two
+  // tile i's softmax state and P tile with all but block 1's last four
   // exponent stages and the finish done, and sacc[1] holds tile i's block-1
   // scores; leaving, the same holds for tile i+1.
   auto pipe_step_fs = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, SmState& st, bool& jumped,
