@@ -30,13 +30,25 @@
  * slot j % 64, of kv_cache [num_blocks, 64, 576] (row-major, 576 contiguous).
  * Only block_size = 64 is supported.
  *
- * Split-KV.  A call may cut each sequence's tokens into num_kv_splits
- * page-aligned chunks, write one fp32 partial per (b, row, split) into the
+ * Split-KV.  A call may cut each sequence's tokens into up to num_kv_splits
+ * page-aligned pieces, write one fp32 partial per (b, row, piece) into the
  * caller's workspace [B, T*H, splits, 513] (512 normalized outputs, then the
- * chunk's lse) and merge them by log-sum-exp in a second kernel, as in the
+ * piece's lse) and merge them by log-sum-exp in a second kernel, as in the
  * two-stage Triton MLA decode (vLLM PR #46819 digest, "Implementation"
  * items 1-3).  With one split the first kernel writes out and lse itself
  * and the workspace is not touched.
+ *   A dense call with more than one split whose batch (at most 1024
+ * sequences) is smaller than the number of pieces one round of resident
+ * workgroups holds is cut by the actual lengths, on the device: every
+ * sequence of n pages becomes k = max(1, ceil(n / c)) pieces of floor(n / k)
+ * or ceil(n / k) pages, with one piece length c for the batch: the smallest
+ * that keeps the batch within that number of pieces, and at least
+ * ceil(longest / splits) pages.  A long
+ * sequence of a mixed batch thus gets more pieces than a short one, and all
+ * pieces are about equally long.  Slots past a sequence's k-th get lse =
+ * -inf and no outputs.  Other calls cut fixed chunks of
+ * ceil(ceil(max_seq_len / 64) / splits) pages.  Either way the merged result
+ * is the same attention; rounding differs with the cut.
  *
  * Conventions shared by every entry point:
  *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
@@ -62,7 +74,8 @@
  *    [0, num_blocks) read as zero vectors, and block-table slots past a
  *    sequence's last page are never read.  seq_lens[b] must not exceed
  *    max_seq_len (the host bound that sizes the splits); tokens beyond
- *    num_kv_splits chunks of the bound are not attended.
+ *    num_kv_splits chunks of the bound (beyond the bound itself, when the
+ *    device cuts the pieces) are not attended.
  *  - out and lse may not alias any input or the workspace.
  *
  * Two-stage use.  A decode call with out = NULL and lse = NULL stops after
@@ -105,13 +118,18 @@ enum { MLA_OUT_BF16 = 0, MLA_OUT_F32 = 1 };
 const char* mla_status_string(mla_status_t status);
 
 /*
- * Split count the library picks for a call when num_kv_splits = 0.  Work
- * units are (sequence, row block, split).  Each candidate row-block width
- * and split count is costed as the bytes it moves (the KV once per row block,
- * plus the fp32 partials written and read back when split) divided by how
- * fully its units occupy the chip's workgroup slots; the cheapest wins.
- * Deterministic in its arguments; topk = 0 means a dense call, otherwise a
- * sparse call with that K.  Returns 0 on invalid arguments.
+ * Split count (partial slots per sequence) the library picks for a call when
+ * num_kv_splits = 0.  Work units are (sequence, row block, split).  Each
+ * candidate row-block width and split count is costed, for sequences of
+ * max_seq_len, as the bytes it moves (the KV once per row block, plus the
+ * fp32 partials written and read back when split) divided by how fully its
+ * units occupy the chip's workgroup slots; the cheapest wins.  A dense call
+ * whose pieces are cut by the actual lengths (see Split-KV above) then gets
+ * twice that many slots (at most one per page), so that long sequences of a
+ * mixed batch can take more pieces.  Passing the returned count explicitly
+ * gives the same launch.  Deterministic in its arguments; topk = 0 means a
+ * dense call, otherwise a sparse call with that K.  Returns 0 on invalid
+ * arguments.
  */
 int mla_num_kv_splits(int batch, int q_len, int num_heads, int max_seq_len, int topk,
                       int kv_fp8);
@@ -206,7 +224,9 @@ mla_status_t mla_sparse_decode(const void* q_nope, const void* q_pe, const void*
  * out = sum_s exp(lse_s - lse) * O_s with lse = ln sum_s exp(lse_s), the
  * merge of the two-stage Triton MLA decode (vLLM PR #46819 digest,
  * "Implementation" items 1-3); rows whose splits are all empty get 0 and
- * -inf.  num_kv_splits in [1, MLA_MAX_KV_SPLITS].
+ * -inf.  The outputs of a split whose weight exp(lse_s - lse) is zero (an
+ * empty one above all) are not read, so they may hold anything.
+ * num_kv_splits in [1, MLA_MAX_KV_SPLITS].
  */
 mla_status_t mla_merge_partials(const float* workspace, int64_t rows, int num_kv_splits, void* out,
                                 int out_dtype, float* lse, void* stream);

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -21,8 +22,13 @@ struct Plan {
   int rg = 1;       // waves per workgroup (32 rows each)
   int n_rb = 1;     // row blocks per (sequence, split)
   int n_hb = 1;     // sparse: head blocks per draft token
-  int S = 1;        // KV splits
+  int S = 1;        // KV splits (partial slots per sequence)
   int chunk = 1;    // dense: pages per split; sparse: indices per split
+  bool balance = false;   // dense, S > 1: length-balanced pieces (cut on the device)
+  int n_target = 0;       // balanced: pieces one round of workgroups holds
+  int max_pages = 0;      // dense: pages of max_seq_len
+  int unit_pages = 0;     // dense: a work unit's pages when every sequence is max_seq_len long
+  int64_t grid_units = 0; // work units the launch covers
   size_t ws_bytes = 0;
 };
 
@@ -37,6 +43,18 @@ int wg_per_cu(int rg) { return rg == 4 ? 1 : 2; }
 bool dims_ok(int B, int T, int H, int max_seq_len, int topk) {
   return B >= 0 && B <= (1 << 20) && T >= 1 && T <= MLA_MAX_Q_LEN && H >= 1 && H <= 1024 &&
          max_seq_len >= 0 && max_seq_len <= (1 << 26) && topk >= 0 && topk <= (1 << 24);
+}
+
+// The piece length (pages) the device picks for a batch whose sequences are
+// all n_pages long: the smallest c >= ceil(n_pages / S), capped by the LDS
+// page table, for which B * ceil(n_pages / c) <= n_target (the largest when
+// none qualifies).  Used to choose the kernel variant for the pieces' length.
+int balanced_length(int B, int n_pages, int S, int n_target) {
+  const int lo = std::max(1, ceil_div(n_pages, S));
+  const int hi = std::max(lo, std::min(n_pages, kDensePagesMax));
+  for (int c = lo; c <= hi; c++)
+    if ((int64_t)B * std::max(1, ceil_div(n_pages, c)) <= n_target) return c;
+  return hi;
 }
 
 // Split planning.  Work unit = (sequence, row block, split).  Every
@@ -96,11 +114,36 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
     c = ceil_div(c, 64) * 64;
     if (c > kSparseChunkMax) return false;
     p.chunk = c;
+    p.grid_units = (int64_t)B * S * p.n_rb;
   } else {
     p.n_rb = ceil_div(p.R, rb_rows);
-    const int max_pages = ceil_div(max_seq_len, MLA_BLOCK_SIZE);
+    p.max_pages = max_pages;
+    // With more than one split, the device cuts the actual lengths into
+    // near-equal pieces (balanced_piece in the kernels).  That pays off when
+    // the batch has fewer sequences than one round of workgroups holds
+    // (otherwise every sequence stays one piece).  The split count costed
+    // above assumes every sequence is max_seq_len long; in a mixed batch a
+    // long sequence may need more pieces than that, so the library's own
+    // choice gives each sequence twice the slots.
+    const int64_t slots = (int64_t)kNumCUs * wg_per_cu(rg);
+    const int n_target = (int)std::max<int64_t>(1, slots / p.n_rb);
+    p.balance = S > 1 && B <= mla::kBalanceMaxBatch && B < n_target;
+    if (p.balance && req_splits == 0) S = std::max(S, std::min(2 * S, s_max));
     p.chunk = max_pages > 0 ? ceil_div(max_pages, S) : 1;
     if (p.chunk > kDensePagesMax) return false;
+    p.unit_pages = p.chunk;
+    p.grid_units = (int64_t)B * S * p.n_rb;
+    if (p.balance) {
+      p.n_target = n_target;
+      p.unit_pages = balanced_length(B, max_pages, S, p.n_target);
+      // Pieces never exceed B * S; they stay within n_target whenever one
+      // piece per sequence (at the largest length the page table holds)
+      // already does.
+      const int top = std::max(1, std::min(max_pages, kDensePagesMax));
+      const int64_t worst = (int64_t)B * ceil_div(std::max(max_pages, 1), top);
+      const int64_t pieces = worst <= p.n_target ? std::min<int64_t>(p.n_target, (int64_t)B * S) : (int64_t)B * S;
+      p.grid_units = ceil_div(pieces, 8) * 8 * (int64_t)p.n_rb;
+    }
   }
   p.S = S;
   p.ws_bytes = S > 1 ? (size_t)B * p.R * S * kPartialWidth * sizeof(float) : 0;
@@ -161,7 +204,10 @@ mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv
   p.n_hb = pl.n_hb;
   p.chunk = pl.chunk;
   p.S = pl.S;
-  const int64_t units = (int64_t)B * pl.S * pl.n_rb;
+  p.balance = pl.balance ? 1 : 0;
+  p.n_target = pl.n_target;
+  p.max_pages = pl.max_pages;
+  const int64_t units = pl.grid_units;
   if (units > (int64_t)1 << 30) return MLA_ERR_INVALID_ARGUMENT;
   p.n_units = (int)units;
   const float log2e = 1.4426950408889634f;
@@ -173,7 +219,8 @@ mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv
   p.ws = pl.S > 1 ? (float*)workspace : nullptr;
   const int grid = (int)((units + 7) / 8 * 8);
   hipStream_t st = (hipStream_t)stream;
-  const bool resid = fp8 && (int64_t)pl.chunk * MLA_BLOCK_SIZE <= mla::kFp8ResidualMaxUnitTokens;
+  const int64_t unit_tokens = (int64_t)(sparse ? pl.chunk : pl.unit_pages * MLA_BLOCK_SIZE);
+  const bool resid = fp8 && unit_tokens <= mla::kFp8ResidualMaxUnitTokens;
   if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, resid, grid, st) != hipSuccess) return MLA_ERR_HIP;
   if (pl.S > 1 && !stage1_only) {
     mla::MergeParams m{};

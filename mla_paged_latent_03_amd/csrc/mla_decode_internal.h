@@ -13,6 +13,7 @@ constexpr int kPartialWidth = kLatentDim + 1;   // normalized outputs, then the 
 constexpr int kSparseChunkMax = 1024;           // top-k entries one workgroup handles
 constexpr int kDensePagesMax = 1024;            // pages one workgroup handles (65536 tokens)
 constexpr int kNumCUs = 256;                    // MI355X compute units
+constexpr int kBalanceMaxBatch = 1024;          // largest batch whose split lengths are balanced on the device
 
 struct PartialParams {
   const uint8_t* q_nope;        // [B, T, H, 512] bf16 or e4m3 bytes
@@ -25,8 +26,11 @@ struct PartialParams {
   int n_rb;                     // row blocks per (sequence, split)
   int n_hb;                     // sparse: head blocks per draft token
   int chunk;                    // dense: pages per split; sparse: indices per split
-  int S;                        // splits
+  int S;                        // splits (partial slots per sequence)
   int n_units;                  // B * S * n_rb
+  int balance;                  // dense, S > 1: length-balanced pieces instead of fixed chunks
+  int n_target;                 // balanced: pieces the batch may be cut into (one round of workgroups)
+  int max_pages;                // balanced: pages of max_seq_len (longer sequences are cut there)
   float qk_scale;               // softmax_scale * log2(e) [* q_scale * kv_scale]
   float out_scale;              // kv_scale (fp8) or 1
   void* out;                    // [B, T, H, 512] bf16 / f32 (one split)

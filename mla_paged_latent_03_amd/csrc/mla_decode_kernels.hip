@@ -208,6 +208,165 @@ __device__ inline void mfma_drain(f32x16_t& a, f32x16_t& b) {
 }
 
 // ---------------------------------------------------------------------------
+// Length-balanced pieces (dense calls with more than one split).
+//
+// The host knows only a bound of the sequence lengths, so every workgroup
+// derives the cut from the lengths themselves (the same result in each):
+//  * a sequence of n pages is cut into k = max(1, ceil(n / c)) pieces; piece
+//    i covers pages [i n / k, (i+1) n / k), so its pieces differ by at most a
+//    page and none is longer than c;
+//  * c is the smallest length for which the whole batch needs at most
+//    n_target pieces, n_target being the workgroups the chip holds at once
+//    divided by the row blocks per piece: the pieces then run in one round
+//    and are about equally long, whatever the spread of the lengths.  c is
+//    at least ceil(longest / S) (a sequence has S partial slots) and at most
+//    the LDS page table's capacity; when no length qualifies, the largest
+//    one is taken;
+//  * pieces are numbered sequence after sequence.
+// Lengths are clamped as the kernel clamps them, and to max_pages.
+struct Piece {
+  int b;          // sequence
+  int k;          // piece of that sequence, which is its partial slot
+  int n;          // pieces of that sequence
+  int pg0, pg1;   // pages [pg0, pg1) of the sequence
+};
+
+// Row (16-lane) sums and maxima through DPP; a lane then holds its row's
+// result and four lane reads combine the rows.
+__device__ __attribute__((always_inline)) inline int row16_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);   // row_mirror
+  return v;
+}
+__device__ __attribute__((always_inline)) inline int wave_sum_i(int v) {
+  v = row16_sum(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
+__device__ __attribute__((always_inline)) inline int wave_max_i(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// ceil(x / c) for 0 <= x < 2^21 and 1 <= c <= 2^11, rc being 1/c rounded to
+// float: the float quotient is then within 1/4 of the exact one, so a single
+// correction of the truncated value makes it exact.
+__device__ __attribute__((always_inline)) inline int ceil_div_small(int x, int c, float rc) {
+  const int y = x + c - 1;
+  int q = (int)((float)y * rc);
+  const int r = y - q * c;
+  q += r >= c ? 1 : 0;
+  q -= r < 0 ? 1 : 0;
+  return q;
+}
+
+// Lane l holds sequences [l M', l M' + M') with M' = ceil(B / 64) <= M.
+template <int M>
+__device__ __attribute__((always_inline)) inline bool balanced_piece_m(const PartialParams& p, int j, Piece* pc) {
+  const int lane = threadIdx.x & 63;
+  const int m = (p.B + 63) >> 6;
+  const int first = lane * m;
+  const int nv = max(0, min(m, p.B - first));       // sequences of this lane
+  const int cap = p.MB * 64;
+  int pg[M];
+  int tot = 0, mx = 0;
+#pragma unroll
+  for (int e = 0; e < M; e++) {
+    int n = 0;
+    if (e < nv) {
+      int L = p.seq_lens[first + e];
+      L = L < 0 ? 0 : (L > cap ? cap : L);
+      n = min((L + 63) >> 6, p.max_pages);
+    }
+    pg[e] = n;
+    tot += n;
+    mx = max(mx, n);
+  }
+  tot = wave_sum_i(tot);
+  mx = wave_max_i(mx);
+
+  auto count = [&](int c) {
+    const float rc = 1.0f / (float)c;
+    int s = 0;
+#pragma unroll
+    for (int e = 0; e < M; e++) s += e < nv ? max(1, ceil_div_small(pg[e], c, rc)) : 0;
+    return wave_sum_i(s);
+  };
+  const int S = p.S, NT = p.n_target;
+  int lo = max(1, (mx + S - 1) / S);
+  lo = max(lo, min((tot + NT - 1) / NT, kDensePagesMax));
+  int hi = max(lo, min(mx, kDensePagesMax));
+  // sum max(1, ceil(n / c)) <= tot / c + B, so c >= tot / (NT - B) qualifies
+  if (NT > p.B) hi = max(lo, min(hi, (tot + (NT - p.B) - 1) / (NT - p.B)));
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (count(mid) <= NT) hi = mid;
+    else lo = mid + 1;
+  }
+  const int c = lo;
+
+  // Pieces per sequence, their running count over the lanes, and the lane
+  // that holds piece j.
+  const float rc = 1.0f / (float)c;
+  int kb[M];
+  int ls = 0;
+#pragma unroll
+  for (int e = 0; e < M; e++) {
+    kb[e] = e < nv ? max(1, ceil_div_small(pg[e], c, rc)) : 0;
+    ls += kb[e];
+  }
+  int inc = ls;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(inc, d);
+    if (lane >= d) inc += t;
+  }
+  const int total = __builtin_amdgcn_readlane(inc, 63);
+  if (j >= total) return false;
+  const int excl = inc - ls;
+  const uint64_t own = __builtin_amdgcn_ballot_w64(j >= excl && j < inc);
+  const int owner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(own));
+  int rem = j - excl, fb = 0, fk = 0, fn = 1, fp = 0;
+  bool found = false;
+#pragma unroll
+  for (int e = 0; e < M; e++) {
+    if (!found && e < nv) {
+      if (rem < kb[e]) {
+        found = true;
+        fb = first + e;
+        fk = rem;
+        fn = kb[e];
+        fp = pg[e];
+      } else {
+        rem -= kb[e];
+      }
+    }
+  }
+  pc->b = __builtin_amdgcn_readlane(fb, owner);
+  pc->k = __builtin_amdgcn_readlane(fk, owner);
+  pc->n = __builtin_amdgcn_readlane(fn, owner);
+  const int n_pg = __builtin_amdgcn_readlane(fp, owner);
+  pc->pg0 = pc->k * n_pg / pc->n;
+  pc->pg1 = (pc->k + 1) * n_pg / pc->n;
+  return true;
+}
+
+__device__ __attribute__((always_inline)) inline bool balanced_piece(const PartialParams& p, int j, Piece* pc) {
+  const int m = (p.B + 63) >> 6;
+  if (m <= 1) return balanced_piece_m<1>(p, j, pc);
+  if (m <= 2) return balanced_piece_m<2>(p, j, pc);
+  if (m <= 4) return balanced_piece_m<4>(p, j, pc);
+  if (m <= 8) return balanced_piece_m<8>(p, j, pc);
+  return balanced_piece_m<kBalanceMaxBatch / 64>(p, j, pc);
+}
+
+// ---------------------------------------------------------------------------
 // Split-KV partial kernel.
 //   FP8    : e4m3 cache and query (else bf16)
 //   SPARSE : visible tokens from top-k index lists (else dense causal)
@@ -253,15 +412,35 @@ mla_partial_kernel(const PartialParams p) {
   const int h = lane >> 5;       // which half of the wave
   const int l32 = lane & 31;     // MFMA column = query row within the wave
 
-  // ---- work unit: XCD-aware renumbering of the linear workgroup id so that
-  // consecutive units (row blocks of one (sequence, split)) share an XCD.
-  const int nwg = gridDim.x;     // multiple of 8
-  const int u = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-  if (u >= p.n_units) return;
-  const int rb = u % p.n_rb;
-  const int bs = u / p.n_rb;
-  const int split = bs % p.S;
-  const int b = bs / p.S;
+  // ---- work unit.  Consecutive workgroup ids land on consecutive XCDs
+  // (eight, each with its own L2); the row blocks of one (sequence, split)
+  // read the same KV and are kept on one XCD.
+  int rb, split, b, n_split, bal_pg0 = 0, bal_pg1 = 0;
+  if (!SPARSE && p.balance) {
+    // Length-balanced pieces, dealt round-robin to the XCDs: piece j runs on
+    // XCD j mod 8, so every XCD gets an equal share of near-equal pieces.
+    const int i = blockIdx.x >> 3;
+    rb = i % p.n_rb;
+    const int j = (i / p.n_rb) * 8 + (blockIdx.x & 7);
+    Piece pc;
+    if (!balanced_piece(p, j, &pc)) return;
+    b = pc.b;
+    split = pc.k;
+    n_split = pc.n;
+    bal_pg0 = pc.pg0;
+    bal_pg1 = pc.pg1;
+  } else {
+    // Fixed chunks: unit u = (sequence, split, row block), renumbered so that
+    // consecutive units share an XCD.
+    const int nwg = gridDim.x;     // multiple of 8
+    const int u = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    if (u >= p.n_units) return;
+    rb = u % p.n_rb;
+    const int bs = u / p.n_rb;
+    split = bs % p.S;
+    b = bs / p.S;
+    n_split = p.S;
+  }
 
   int L = ((const CONST_AS int32_t*)p.seq_lens)[b];
   L = L < 0 ? 0 : (L > p.MB * 64 ? p.MB * 64 : L);
@@ -291,8 +470,8 @@ mla_partial_kernel(const PartialParams p) {
     n_tiles = (idx_count + K::kTileTok - 1) / K::kTileTok;
   } else {
     const int n_pages = (L + 63) >> 6;
-    page0 = split * p.chunk;
-    const int p1 = min(page0 + p.chunk, n_pages);
+    page0 = p.balance ? bal_pg0 : split * p.chunk;
+    const int p1 = p.balance ? bal_pg1 : min(page0 + p.chunk, n_pages);
     n_unit_pages = p1 > page0 ? p1 - page0 : 0;
     tok_begin = page0 * 64;
     const int tok_end = n_unit_pages > 0 ? min(p1 * 64, L) : tok_begin;
@@ -366,7 +545,9 @@ mla_partial_kernel(const PartialParams p) {
       d.n_valid = real ? K::kTileTok : 0;
     } else {
       const int tok0 = tok_begin + (real ? i : 0) * K::kTileTok;
-      const int pg = n_tiles > 0 ? table[(tok0 >> 6) - page0] : -1;   // same address in every lane
+      // Same address in every lane; taken into a scalar register at once so
+      // that the descriptor arithmetic below stays on the scalar unit.
+      const int pg = n_tiles > 0 ? __builtin_amdgcn_readfirstlane(table[(tok0 >> 6) - page0]) : -1;
       const int n_valid = (real && pg >= 0) ? min(K::kTileTok, L - tok0) : 0;
       d.rsrc = buffer_rsrc(p.kv + ((int64_t)(pg >= 0 ? pg : 0) * 64 + (tok0 & 63)) * K::kRowBytes,
                            (uint32_t)(n_valid * K::kRowBytes));
@@ -1212,7 +1393,13 @@ mla_partial_kernel(const PartialParams p) {
     if (p.S == 1) {
       if (p.lse) p.lse[qrow] = lse_v;
     } else {
-      p.ws[(qrow * p.S + split) * (int64_t)kPartialWidth + 512] = lse_v;
+      float* wl = p.ws + qrow * p.S * (int64_t)kPartialWidth + 512;
+      wl[split * (int64_t)kPartialWidth] = lse_v;
+      // A sequence cut into fewer pieces than it has slots: its last piece
+      // marks the remaining slots empty (lse -inf; their outputs are left
+      // unwritten and the merge does not read them).
+      if (split == n_split - 1)
+        for (int s = n_split; s < p.S; s++) wl[s * (int64_t)kPartialWidth] = -INFINITY;
     }
   };
 
@@ -1265,14 +1452,19 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(const MergeParams p) {
       for (int d = 32; d >= 1; d >>= 1) zs += __shfl_xor(zs, d);
       z += zs;
       // Eight splits at a time: all of a group's loads are issued before any
-      // is used, so their latencies overlap.  (Rows of 513 floats are only
-      // 4-byte aligned, hence single-float loads.)
+      // is used, so their latencies overlap.  A split of weight zero (an
+      // empty one, lse -inf) is not read: its outputs may be undefined.
+      // (Rows of 513 floats are only 4-byte aligned, hence single-float
+      // loads.)
       const int ns = min(64, p.S - s0);
       for (int k0 = 0; k0 < ns; k0 += 8) {
+        float wk[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) wk[k] = __shfl(w, (k0 + k) & 63);   // w is 0 past ns
         float v[8][8];
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-          if (k0 + k < ns) {
+          if (wk[k] != 0.f) {
             const float* src = base + (int64_t)(s0 + k0 + k) * kPartialWidth + 8 * lane;
 #pragma unroll
             for (int c = 0; c < 8; c++) v[k][c] = src[c];
@@ -1280,10 +1472,9 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(const MergeParams p) {
         }
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-          if (k0 + k < ns) {
-            const float wk = __shfl(w, k0 + k);
+          if (wk[k] != 0.f) {
 #pragma unroll
-            for (int c = 0; c < 8; c++) acc[c] += wk * v[k][c];
+            for (int c = 0; c < 8; c++) acc[c] += wk[k] * v[k][c];
           }
         }
       }

@@ -67,10 +67,15 @@ def test_workspace_matches_split_count(lib, B, T, H, L, K, fp8):
 
 
 def test_heuristic_fills_the_chip(lib):
-    # The 80k-token MTP-3 fp8 batch: 64 sequences x 1 row block -> 4 splits = 256 workgroups.
-    assert binding.num_kv_splits(64, 4, 32, 80000, 0, True) == 4
-    # 128 one-wave sequences: 4 splits = 512 workgroups, two per compute unit.
-    assert binding.num_kv_splits(128, 1, 16, 8192, 0, False) == 4
+    # Dense calls: the split count is costed for sequences of max_seq_len and
+    # each sequence then gets twice as many partial slots, so that the device
+    # can cut long sequences of a mixed batch into more, equal pieces.
+    # The 80k-token MTP-3 fp8 batch: 64 sequences x 1 row block -> 4 pieces each = 256 workgroups.
+    assert binding.num_kv_splits(64, 4, 32, 80000, 0, True) == 8
+    # 128 one-wave sequences: 4 pieces each = 512 workgroups, two per compute unit.
+    assert binding.num_kv_splits(128, 1, 16, 8192, 0, False) == 8
+    # Never more slots than pages.
+    assert binding.num_kv_splits(2, 1, 16, 300, 0, False) == 5
     # Sparse top-2048 over 64 sequences: 4 splits of 512 indices = 256 four-wave workgroups
     # (narrower row blocks would read every gathered row once per block).
     assert binding.num_kv_splits(64, 1, 128, 65536, 2048, False) == 4

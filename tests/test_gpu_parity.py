@@ -204,6 +204,39 @@ def test_maximum_split_count_with_empty_splits():
     check_full(inp, binding.MAX_KV_SPLITS, "256 splits")
 
 
+# ------------------------------------------------------------------ length-balanced pieces
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_skewed_lengths_are_cut_into_balanced_pieces(kv_dtype):
+    """One long sequence among many short, empty and one-token ones: the
+    device cuts the long one into as many pieces as it has slots, the short
+    ones stay whole and mark their other slots empty."""
+    lens = [8192] + [1, 0, 10, 64, 65] * 12 + [130, 3000, 700]
+    inp = wl.make_inputs(len(lens), 16, 1, lens, kv_dtype=kv_dtype, out_dtype="f32", seed=55, poison=True)
+    check_full(inp, 0, "skewed lengths %s" % kv_dtype)
+
+
+@pytest.mark.parametrize("H,T,kv_dtype", [(32, 4, "fp8"), (32, 8, "bf16"), (64, 2, "bf16"), (128, 1, "fp8")])
+def test_mixed_lengths_balanced_pieces_every_row_block(H, T, kv_dtype):
+    inp = wl.make_inputs(12, H, T, (200, 6000), kv_dtype=kv_dtype, out_dtype="f32", seed=56 + H + T, poison=True)
+    check_full(inp, 0, "mixed lengths H=%d T=%d %s" % (H, T, kv_dtype))
+
+
+def test_host_bound_far_above_the_lengths():
+    """max_seq_len four times the longest sequence: the pieces follow the
+    actual lengths, not the bound."""
+    inp = wl.make_inputs(8, 16, 2, (100, 2500), kv_dtype="bf16", out_dtype="f32", seed=57, poison=True)
+    inp.max_len = 4 * inp.max_len
+    check_full(inp, 0, "bound 4x the lengths")
+    check_full(inp, 3, "bound 4x the lengths, three splits")
+
+
+def test_batch_above_the_balanced_limit_uses_fixed_chunks():
+    """More sequences than the device-side cut takes: fixed page chunks."""
+    inp = wl.make_inputs(1040, 16, 1, (1, 400), kv_dtype="bf16", out_dtype="f32", seed=58)
+    check_full(inp, 2, "B=1040 two splits")
+
+
 @pytest.mark.parametrize("H,T,kv_dtype", [(1, 1, "bf16"), (1, 8, "bf16"), (1, 8, "fp8"), (16, 8, "bf16")])
 def test_degenerate_head_counts_and_longest_draft(H, T, kv_dtype):
     inp = wl.make_inputs(3, H, T, [5, 200, 1500], kv_dtype=kv_dtype, out_dtype="f32", seed=54 + H + T, poison=True)
