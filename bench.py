@@ -170,7 +170,11 @@ def main():
         l = None if stage1_only else lse
         inp = sets[calls[0] % len(sets)]
         calls[0] += 1
-        if inp.K > 0:
+        if inp.K > 0 and fp8:
+            binding.mla_sparse_decode_fp8(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens,
+                                          inp.topk_indices, inp.max_seq_len, inp.softmax_scale, inp.q_scale,
+                                          inp.kv_scale, o, l, ws, S, stream)
+        elif inp.K > 0:
             binding.mla_sparse_decode(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens,
                                       inp.topk_indices, inp.max_seq_len, inp.softmax_scale, o, l, ws, S, stream)
         elif fp8:

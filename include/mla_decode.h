@@ -216,6 +216,25 @@ mla_status_t mla_sparse_decode(const void* q_nope, const void* q_pe, const void*
                                size_t workspace_bytes, int num_kv_splits, void* stream);
 
 /*
+ * Top-k sparse fp8 decode: the token lists of mla_sparse_decode over the
+ * e4m3fn cache and query of mla_decode_fp8, with the same per-tensor
+ * q_scale and kv_scale (index_topk per query token, vLLM PR #47327 digest,
+ * "Key code excerpt"; fp8 dequant scales, vLLM PR #41778 digest,
+ * "Implementation" item 1).  A gathered token row is 576 bytes.  Every work
+ * unit holds at most 1024 indices, so the softmax weights always get the
+ * second (residual) fp8 product that carries them to about 2^-8.  Workspace
+ * sized with topk = K and kv_fp8 = 1; other arguments as mla_sparse_decode.
+ */
+mla_status_t mla_sparse_decode_fp8(const void* q_nope, const void* q_pe, const void* kv_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* topk_indices, int topk, int batch, int q_len,
+                                   int num_heads, int num_blocks, int block_size,
+                                   int max_blocks_per_seq, int max_seq_len, float softmax_scale,
+                                   float q_scale, float kv_scale, void* out, int out_dtype,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   int num_kv_splits, void* stream);
+
+/*
  * Second stage alone: log-sum-exp merge of split partials.
  *   workspace  [rows, num_kv_splits, 513] fp32, as a decode call writes it
  *              (rows = B * T * H; per (row, split): 512 normalized outputs

@@ -57,6 +57,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_fp8.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_float, c_float] + common_tail[1:]
     lib.mla_sparse_decode.restype = c_int
     lib.mla_sparse_decode.argtypes = [vp, vp, vp, vp, vp, vp, c_int] + [c_int] * 7 + common_tail
+    lib.mla_sparse_decode_fp8.restype = c_int
+    lib.mla_sparse_decode_fp8.argtypes = ([vp, vp, vp, vp, vp, vp, c_int] + [c_int] * 7 + [c_float, c_float, c_float]
+                                          + common_tail[1:])
     lib.mla_merge_partials.restype = c_int
     lib.mla_merge_partials.argtypes = [vp, ctypes.c_int64, c_int, vp, c_int, vp, vp]
     _lib = lib
@@ -156,6 +159,21 @@ def mla_sparse_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, topk_indice
     _check(st, "mla_sparse_decode")
 
 
+def mla_sparse_decode_fp8(q_nope, q_pe, kv_cache, block_table, seq_lens, topk_indices, max_seq_len, softmax_scale,
+                          q_scale, kv_scale, out, lse=None, workspace=None, num_kv_splits=0, stream=None):
+    """Top-k sparse e4m3 decode (mla_sparse_decode_fp8)."""
+    B, T, H, _ = q_nope.shape
+    NB, P, _ = kv_cache.shape
+    K = topk_indices.shape[2]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().mla_sparse_decode_fp8(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(block_table),
+                                      _ptr(seq_lens), _ptr(topk_indices), K, B, T, H, NB, P, block_table.shape[1],
+                                      int(max_seq_len), float(softmax_scale), float(q_scale), float(kv_scale),
+                                      _ptr(out), _out_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                      int(num_kv_splits), _stream(stream))
+    _check(st, "mla_sparse_decode_fp8")
+
+
 def mla_merge_partials(workspace, rows, num_kv_splits, out, lse=None, stream=None):
     """Second stage alone (mla_merge_partials): LSE merge of [rows, S, 513] partials."""
     st = load().mla_merge_partials(_ptr(workspace), int(rows), int(num_kv_splits), _ptr(out), _out_code(out),
@@ -182,7 +200,11 @@ def decode(inp, num_kv_splits=0, out=None, lse=None, workspace=None, stream=None
     need = workspace_size(B, T, H, msl, K, fp8, num_kv_splits)
     if workspace is None and need > 0:
         workspace = torch.empty((need + 3) // 4, device=dev, dtype=torch.float32)
-    if K > 0:
+    if K > 0 and fp8:
+        mla_sparse_decode_fp8(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, inp.topk_indices,
+                              msl, inp.softmax_scale, inp.q_scale, inp.kv_scale, out, lse, workspace,
+                              num_kv_splits, stream)
+    elif K > 0:
         mla_sparse_decode(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, inp.topk_indices, msl,
                           inp.softmax_scale, out, lse, workspace, num_kv_splits, stream)
     elif fp8:

@@ -153,15 +153,15 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
-enum class Kind { kBf16, kFp8, kSparse };
+enum class Kind { kBf16, kFp8, kSparse, kSparseFp8 };
 
 mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv_cache,
                  const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk_indices,
                  int topk, int B, int T, int H, int NB, int block_size, int MB, int max_seq_len,
                  float softmax_scale, float q_scale, float kv_scale, void* out, int out_dtype, float* lse,
                  void* workspace, size_t workspace_bytes, int num_kv_splits, void* stream) {
-  const bool fp8 = kind == Kind::kFp8;
-  const bool sparse = kind == Kind::kSparse;
+  const bool fp8 = kind == Kind::kFp8 || kind == Kind::kSparseFp8;
+  const bool sparse = kind == Kind::kSparse || kind == Kind::kSparseFp8;
   if (block_size != MLA_BLOCK_SIZE) return MLA_ERR_UNSUPPORTED;
   if (!dims_ok(B, T, H, max_seq_len, sparse ? topk : 0)) return MLA_ERR_INVALID_ARGUMENT;
   if (sparse && topk < 1) return MLA_ERR_INVALID_ARGUMENT;
@@ -309,6 +309,18 @@ mla_status_t mla_sparse_decode(const void* q_nope, const void* q_pe, const void*
   return run(Kind::kSparse, q_nope, q_pe, kv_cache, block_table, seq_lens, topk_indices, topk, batch, q_len,
              num_heads, num_blocks, block_size, max_blocks_per_seq, max_seq_len, softmax_scale, 1.0f, 1.0f, out,
              out_dtype, lse, workspace, workspace_bytes, num_kv_splits, stream);
+}
+
+mla_status_t mla_sparse_decode_fp8(const void* q_nope, const void* q_pe, const void* kv_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* topk_indices, int topk, int batch, int q_len, int num_heads,
+                                   int num_blocks, int block_size, int max_blocks_per_seq, int max_seq_len,
+                                   float softmax_scale, float q_scale, float kv_scale, void* out, int out_dtype,
+                                   float* lse, void* workspace, size_t workspace_bytes, int num_kv_splits,
+                                   void* stream) {
+  return run(Kind::kSparseFp8, q_nope, q_pe, kv_cache, block_table, seq_lens, topk_indices, topk, batch, q_len,
+             num_heads, num_blocks, block_size, max_blocks_per_seq, max_seq_len, softmax_scale, q_scale, kv_scale,
+             out, out_dtype, lse, workspace, workspace_bytes, num_kv_splits, stream);
 }
 
 mla_status_t mla_merge_partials(const float* workspace, int64_t rows, int num_kv_splits, void* out, int out_dtype,

@@ -1535,6 +1535,14 @@ hipError_t launch_partial_kernel(const PartialParams& p, bool fp8, bool sparse, 
       case 2: return launch_partial<false, true, 2, 2>(p, grid, stream);
       case 4: return launch_partial<false, true, 4, 4>(p, grid, stream);
     }
+  } else if (fp8 && sparse && resid) {
+    // A sparse unit holds at most 1024 indices, always short enough for the
+    // residual product.
+    switch (rg) {
+      case 1: return launch_partial<true, true, 1, 2, true>(p, grid, stream);
+      case 2: return launch_partial<true, true, 2, 2, true>(p, grid, stream);
+      case 4: return launch_partial<true, true, 4, 4, true>(p, grid, stream);
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -114,6 +114,9 @@ WORKLOADS = {
                                          out_dtype="bf16", seed=1004),
     "sparse_b64_h128_kv64k_top2048_bf16": dict(B=64, H=128, T=1, seq_lens=[65536] * 64, kv_dtype="bf16",
                                                out_dtype="bf16", topk=2048, seed=1005),
+    # The same top-2048 selection over an e4m3 cache (the fp8 sparse variant).
+    "sparse_b64_h128_kv64k_top2048_fp8": dict(B=64, H=128, T=1, seq_lens=[65536] * 64, kv_dtype="fp8",
+                                              out_dtype="bf16", topk=2048, seed=1006),
 }
 
 

@@ -5,6 +5,7 @@ tails, empty rows, forced split counts, every row-block width and both
 cache dtypes.  Full-size workloads run in the launch configuration the
 benchmark times and compare sampled rows the oracle computes one by one.
 """
+import dataclasses
 import math
 import sys
 
@@ -257,8 +258,21 @@ def test_sparse_shapes(H, T, lens, K, splits):
     check_full(inp, splits, "sparse H=%d K=%d" % (H, K))
 
 
-def test_sparse_out_of_range_and_duplicate_indices():
-    inp = wl.make_inputs(2, 16, 1, [300, 300], kv_dtype="bf16", out_dtype="f32", topk=128, seed=14)
+@pytest.mark.parametrize("H,T,lens,K,splits", [
+    (16, 1, [100, 3000], 256, 0),      # first sequence shorter than K: -1 padding
+    (16, 1, [100, 3000], 256, 2),
+    (128, 1, [5000, 70], 512, 0),
+    (64, 2, [900, 2500], 192, 0),      # MTP with per-token index lists
+    (32, 1, [4100], 4096, 0),          # K above one workgroup's index table: forced splits
+])
+def test_sparse_fp8_shapes(H, T, lens, K, splits):
+    inp = wl.make_inputs(len(lens), H, T, lens, kv_dtype="fp8", out_dtype="f32", topk=K, seed=23 + H, poison=True)
+    check_full(inp, splits, "sparse fp8 H=%d K=%d" % (H, K))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_sparse_out_of_range_and_duplicate_indices(kv_dtype):
+    inp = wl.make_inputs(2, 16, 1, [300, 300], kv_dtype=kv_dtype, out_dtype="f32", topk=128, seed=14)
     idx = inp.topk_indices.clone()
     idx[0, 0, :10] = 7                      # duplicates
     idx[0, 0, 10:20] = 300                  # == L: out of range
@@ -291,15 +305,16 @@ def test_sparse_index_probe_histogram_exact():
     assert torch.allclose(lse.cpu().double(), torch.full_like(lse.cpu().double(), math.log(n)), atol=1e-6)
 
 
-def test_sparse_all_positions_equals_dense():
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_sparse_all_positions_equals_dense(kv_dtype):
     L, K = 300, 512
-    inp = wl.make_inputs(1, 32, 1, [L], kv_dtype="bf16", out_dtype="f32", topk=K, seed=16)
+    inp = wl.make_inputs(1, 32, 1, [L], kv_dtype=kv_dtype, out_dtype="f32", topk=K, seed=16)
     o_s, l_s = run_case(inp, 0, "sparse all positions")
-    dense = wl.DecodeInputs(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, None, "bf16", "f32",
-                            inp.softmax_scale)
+    dense = dataclasses.replace(inp, topk_indices=None)
     o_d, l_d = run_case(dense, 0, "dense twin")
-    # Same tokens in another order: equal up to bf16 rounding of P.
-    assert torch.max(torch.abs(o_s - o_d)).item() < 1e-2
+    # Same tokens in another order: equal up to the rounding of P (bf16, or
+    # e4m3 plus its residual).
+    assert torch.max(torch.abs(o_s - o_d)).item() < (1e-2 if kv_dtype == "bf16" else 3e-2)
     assert torch.max(torch.abs(l_s - l_d)).item() < 1e-5
 
 
@@ -315,12 +330,13 @@ FOUR_WAVE = [
     ("fp8", 256, 32, 4, (3, 700), 0),
     ("fp8", 256, 128, 1, (32, 330), 0),
     ("sparse", 256, 128, 1, (100, 900), 96),
+    ("sparse_fp8", 256, 128, 1, (100, 900), 96),
 ]
 
 
 @pytest.mark.parametrize("kind,B,H,T,lens,K", FOUR_WAVE)
 def test_four_wave_variants(kind, B, H, T, lens, K):
-    kv_dtype = "fp8" if kind == "fp8" else "bf16"
+    kv_dtype = "fp8" if kind in ("fp8", "sparse_fp8") else "bf16"
     inp = wl.make_inputs(B, H, T, lens, kv_dtype=kv_dtype, out_dtype="f32", topk=K or None, seed=31 + B + H + T,
                          poison=True)
     assert binding.launch_waves(B, T, H, inp.max_len, K, kv_dtype == "fp8") == 4
@@ -352,11 +368,12 @@ def _plant_large_logit(inp, pos):
     ("bf16", 256, 32, 4, 4), ("bf16", 256, 128, 1, 4), ("bf16", 4, 16, 1, 1), ("bf16", 512, 64, 1, 2),
     ("fp8", 256, 32, 4, 4), ("fp8", 4, 16, 1, 1),
     ("sparse", 256, 128, 1, 4), ("sparse", 4, 16, 1, 1),
+    ("sparse_fp8", 256, 128, 1, 4), ("sparse_fp8", 4, 16, 1, 1),
 ])
 def test_large_logit_jump_reruns_against_exact_maximum(kind, B, H, T, waves):
     L, pos = 300, 150
-    kv_dtype = "fp8" if kind == "fp8" else "bf16"
-    K = 96 if kind == "sparse" else 0
+    kv_dtype = "fp8" if kind in ("fp8", "sparse_fp8") else "bf16"
+    K = 96 if kind.startswith("sparse") else 0
     inp = wl.make_inputs(B, H, T, [L] * B, kv_dtype=kv_dtype, out_dtype="f32", topk=K or None, seed=41 + B + H)
     if K:
         inp.topk_indices[:, :, K // 2] = pos    # the planted position sits in the second index tile
@@ -398,7 +415,7 @@ def test_hip_graph_replay_matches_eager():
 # ------------------------------------------------------------------ full-size workloads (sampled rows)
 
 FULL = ["r1_b128_h16_kv1k-8k_bf16", "mtp3_b64_h32_kv80k_fp8", "mtp7_b32_h128_kv16k-32k_bf16",
-        "sparse_b64_h128_kv64k_top2048_bf16"]
+        "sparse_b64_h128_kv64k_top2048_bf16", "sparse_b64_h128_kv64k_top2048_fp8"]
 
 
 @pytest.mark.parametrize("name", FULL)
