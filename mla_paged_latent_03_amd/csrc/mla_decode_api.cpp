@@ -25,6 +25,7 @@ struct Plan {
   int S = 1;        // KV splits (partial slots per sequence)
   int chunk = 1;    // dense: pages per split; sparse: indices per split
   bool balance = false;   // dense, S > 1: length-balanced pieces (cut on the device)
+  bool lpt = false;       // balanced over two rounds of workgroups, pieces numbered longest first
   int n_target = 0;       // balanced: pieces one round of workgroups holds
   int max_pages = 0;      // dense: pages of max_seq_len
   int unit_pages = 0;     // dense: a work unit's pages when every sequence is max_seq_len long
@@ -100,6 +101,7 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
       }
     }
   }
+  const int S_model = S;
   if (req_splits > 0) S = req_splits;
   if (S < s_min) {
     if (req_splits > 0) return false;   // the split would exceed the LDS table
@@ -129,12 +131,27 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
     const int n_target = (int)std::max<int64_t>(1, slots / p.n_rb);
     p.balance = S > 1 && B <= mla::kBalanceMaxBatch && B < n_target;
     if (p.balance && req_splits == 0) S = std::max(S, std::min(2 * S, s_max));
+    // One round of whole sequences (S = 1) is as long as the longest
+    // sequence.  When the row blocks make the work matrix-bound (at least
+    // four per sequence) and the batch fills one round but not two, the
+    // library's own plan instead cuts the batch into pieces for two rounds
+    // and numbers them longest first: the workgroup slots that finish their
+    // first piece early take the shortest pieces, so the slots end close to
+    // the mean length (for lengths spread over a factor of two, about 0.84
+    // of the longest).  The cost is the partials of two splits per row,
+    // small next to the products over the piece.  An explicit split count
+    // of 2 (what the library reports for such a call) takes the same plan.
+    if (!p.balance && S_model == 1 && (req_splits == 0 || req_splits == 2) && p.n_rb >= 4 && B >= n_target &&
+        B < 2 * n_target && B <= 64 && max_pages >= 2 && s_max >= 2) {
+      p.balance = p.lpt = true;
+      S = 2;
+    }
     p.chunk = max_pages > 0 ? ceil_div(max_pages, S) : 1;
     if (p.chunk > kDensePagesMax) return false;
     p.unit_pages = p.chunk;
     p.grid_units = (int64_t)B * S * p.n_rb;
     if (p.balance) {
-      p.n_target = n_target;
+      p.n_target = p.lpt ? 2 * n_target : n_target;
       p.unit_pages = balanced_length(B, max_pages, S, p.n_target);
       // Pieces never exceed B * S; they stay within n_target whenever one
       // piece per sequence (at the largest length the page table holds)
@@ -206,6 +223,7 @@ mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv
   p.S = pl.S;
   p.balance = pl.balance ? 1 : 0;
   p.n_target = pl.n_target;
+  p.lpt = pl.lpt ? 1 : 0;
   p.max_pages = pl.max_pages;
   const int64_t units = pl.grid_units;
   if (units > (int64_t)1 << 30) return MLA_ERR_INVALID_ARGUMENT;

@@ -222,7 +222,10 @@ __device__ inline void mfma_drain(f32x16_t& a, f32x16_t& b) {
 //    at least ceil(longest / S) (a sequence has S partial slots) and at most
 //    the LDS page table's capacity; when no length qualifies, the largest
 //    one is taken;
-//  * pieces are numbered sequence after sequence.
+//  * pieces are numbered sequence after sequence, or, for a batch of at most
+//    64 sequences cut for two rounds of workgroups (lpt), longest piece
+//    first, which is the longest-processing-time-first order for the
+//    hardware's in-order dispatch of workgroups to free slots.
 // Lengths are clamped as the kernel clamps them, and to max_pages.
 struct Piece {
   int b;          // sequence
@@ -320,6 +323,31 @@ __device__ __attribute__((always_inline)) inline bool balanced_piece_m(const Par
   for (int e = 0; e < M; e++) {
     kb[e] = e < nv ? max(1, ceil_div_small(pg[e], c, rc)) : 0;
     ls += kb[e];
+  }
+  if constexpr (M == 1) {
+    if (p.lpt) {
+      // Longest first: piece slots go to the sequences in decreasing order
+      // of their piece length (ties: lower sequence first), so the longest
+      // pieces start in the first round of workgroups and the slots that
+      // free up early take the shortest ones.  Lane b holds sequence b.
+      const int len = nv > 0 ? (pg[0] + kb[0] - 1) / kb[0] : -1;
+      int rank = 0;
+      for (int o = 0; o < p.B; o++) {
+        const int len_o = __builtin_amdgcn_readlane(len, o);
+        const int kb_o = __builtin_amdgcn_readlane(kb[0], o);
+        rank += (len_o > len || (len_o == len && o < lane)) ? kb_o : 0;
+      }
+      const uint64_t own1 = __builtin_amdgcn_ballot_w64(nv > 0 && j >= rank && j < rank + kb[0]);
+      if (own1 == 0) return false;
+      const int owner1 = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(own1));
+      pc->b = owner1;
+      pc->k = j - __builtin_amdgcn_readlane(rank, owner1);
+      pc->n = __builtin_amdgcn_readlane(kb[0], owner1);
+      const int n_pg1 = __builtin_amdgcn_readlane(pg[0], owner1);
+      pc->pg0 = pc->k * n_pg1 / pc->n;
+      pc->pg1 = (pc->k + 1) * n_pg1 / pc->n;
+      return true;
+    }
   }
   int inc = ls;
 #pragma unroll
@@ -703,11 +731,14 @@ mla_partial_kernel(const PartialParams p) {
   f32x16_t oacc[16];
   // fp8: ones x P^T, the row sum of the rounded weights, normalizes O, so
   // that the up to 2^-4 rounding of each weight cancels.  bf16 weights are
-  // rounded to 2^-9, and O is normalized by the exact fp32 sum l_f instead.
+  // rounded to 2^-9; their row sum l_r comes from dot products of the
+  // packed weights with ones (fp32 accumulation), so that for bf16 too the
+  // numerator and the denominator of O hold the same rounded weights.
   f32x16_t lsum;
   float m_ref = kNegBig;
   float m_seen = -INFINITY;        // running lane maximum, for the second pass
   float l_f = 0.f;                 // this half's sum of the unrounded weights (gives lse)
+  float l_r = 0.f;                 // bf16: this half's sum of the rounded weights (normalizes O)
   const float c_qk = p.qk_scale;   // softmax_scale * log2(e) [* q_scale * kv_scale]
   const int e8m0_one = 127;        // E8M0 scale 2^0 (a VGPR operand of the inline-asm products)
 
@@ -779,6 +810,7 @@ mla_partial_kernel(const PartialParams p) {
     float mr[K::kTokBlocks];     // the row's maximum (feature-split stages)
     float shift[K::kTokBlocks];  // exponent offset applied to the block's scaled scores
     float psum[K::kTokBlocks];   // this lane's sum of the block's unrounded weights
+    float prsum[K::kTokBlocks];  // bf16: this lane's sum of the block's rounded weights
     int sc[K::kTokBlocks];       // fp8: E8M0 scale of the block's weights
   };
 
@@ -834,6 +866,7 @@ mla_partial_kernel(const PartialParams p) {
       st.sc[tb] = 0;
     }
     st.psum[tb] = 0.f;
+    st.prsum[tb] = 0.f;
   };
   // Stage "exponents of registers 4d .. 4d+3 of token block tb".
   auto sm_exp = [&](f32x16_t (&sacc)[K::kTokBlocks], int tb, int d, SmState& st, PTile& pt) {
@@ -869,6 +902,13 @@ mla_partial_kernel(const PartialParams p) {
       int wlo = __builtin_bit_cast(int, lo), whi = __builtin_bit_cast(int, hi);
       pin(wlo);
       pin(whi);
+      const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+      st.prsum[tb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, whi), one2,
+                                                     __builtin_amdgcn_fdot2_f32_bf16(
+                                                         __builtin_bit_cast(bf16x2_t, wlo), one2, st.prsum[tb],
+                                                         false),
+                                                     false);
+      pin(st.prsum[tb]);
       pt.pb[2 * d] = wlo;
       pt.pb[2 * d + 1] = whi;
     }
@@ -884,6 +924,7 @@ mla_partial_kernel(const PartialParams p) {
     } else {
       pt.sc = pt.scl = 0;
       l_f += st.psum[0];
+      l_r += st.prsum[0];
     }
   };
   // Stage k of token block tb's softmax (compile-time k once loops are
@@ -1207,6 +1248,7 @@ mla_partial_kernel(const PartialParams p) {
     for (int fb = 0; fb < 16; fb++) oacc[fb] = f32x16_t{};
     lsum = f32x16_t{};
     l_f = 0.f;
+    l_r = 0.f;
     if (pass == 1) {
       const float mrow = max_across_halves(m_seen);
       m_ref = mrow == -INFINITY ? kNegBig : (FP8 ? ceilf(mrow) : mrow);
@@ -1354,7 +1396,8 @@ mla_partial_kernel(const PartialParams p) {
   // ---- epilogue: normalize, write final output or the split partial
   const float off = FP8 ? 8.f : 0.f;
   l_f = sum_across_halves(l_f);
-  const float l_q = FP8 ? lsum[0] : l_f;   // fp8: every element of a lane's lsum holds its row's sum
+  // fp8: every element of a lane's lsum holds its row's sum of rounded weights.
+  const float l_q = FP8 ? lsum[0] : sum_across_halves(l_r);
   const bool empty = !(l_f > 0.f);
   const float inv = empty ? 0.f : p.out_scale / l_q;
   const float lse_v = empty ? -INFINITY : (m_ref - off + __builtin_amdgcn_logf(l_f)) * kLn2;

@@ -81,7 +81,14 @@ def test_heuristic_fills_the_chip(lib):
     assert binding.num_kv_splits(64, 1, 128, 65536, 2048, False) == 4
     # A chip already full of units takes one split: partials would only add traffic.
     assert binding.num_kv_splits(256, 4, 32, 700, 0, False) == 1
-    assert binding.num_kv_splits(32, 8, 128, 32768, 0, False) == 1
+    assert binding.num_kv_splits(256, 8, 128, 32768, 0, False) == 1
+    # A matrix-bound batch (eight row blocks per sequence) that fills one round
+    # of workgroups but not two: two pieces per sequence, run longest first.
+    assert binding.num_kv_splits(32, 8, 128, 32768, 0, False) == 2
+    assert binding.num_kv_splits(63, 8, 128, 32768, 0, False) == 2
+    # ... but not once the batch fills two rounds, nor with fewer than four row blocks.
+    assert binding.num_kv_splits(64, 8, 128, 32768, 0, False) == 1
+    assert binding.num_kv_splits(128, 2, 128, 32768, 0, False) == 1
     # A top-k list longer than one workgroup's index table forces splits.
     assert binding.num_kv_splits(1, 1, 16, 10000, 5000, False) >= 5
 

@@ -223,6 +223,21 @@ def test_mixed_lengths_balanced_pieces_every_row_block(H, T, kv_dtype):
     check_full(inp, 0, "mixed lengths H=%d T=%d %s" % (H, T, kv_dtype))
 
 
+@pytest.mark.parametrize("B,H,T,lens,kv_dtype", [
+    (64, 128, 4, (0, 700), "bf16"),      # four row blocks, 64 slots per round: 64 sequences
+    (64, 64, 8, (1, 900), "fp8"),
+    (32, 128, 8, (300, 1500), "bf16"),   # eight row blocks, 32 slots per round
+    (40, 128, 8, [0, 1, 64, 65, 2000] * 8, "fp8"),
+])
+def test_two_rounds_longest_first(B, H, T, lens, kv_dtype):
+    """A matrix-bound batch that fills one round of workgroups but not two
+    is cut into two pieces per sequence and run longest piece first."""
+    inp = wl.make_inputs(B, H, T, lens, kv_dtype=kv_dtype, out_dtype="f32", seed=60 + B + H + T, poison=True)
+    assert binding.num_kv_splits(B, T, H, inp.max_len, 0, kv_dtype == "fp8") == 2
+    check_full(inp, 0, "two rounds longest first B=%d H=%d T=%d %s" % (B, H, T, kv_dtype))
+    check_full(inp, 2, "two rounds longest first, explicit 2 splits")
+
+
 def test_host_bound_far_above_the_lengths():
     """max_seq_len four times the longest sequence: the pieces follow the
     actual lengths, not the bound."""
