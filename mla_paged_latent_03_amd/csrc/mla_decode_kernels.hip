@@ -1431,6 +1431,46 @@ mla_partial_kernel(const PartialParams p) {
         for (int c = 0; c < 4; c++) w[8 * a4 + c] = acc[4 * a4 + c] * iv;
     }
   };
+  // Split partials of four-wave blocks leave through LDS.  In the
+  // accumulator layout one store instruction would touch 32 rows (two
+  // 16-byte pieces each); staged as [32 rows][128 features] in the (now
+  // idle) tile ring, each wave then writes every row's 128 features as two
+  // fully coalesced 256-byte stores.  `acc` holds one lane's four feature
+  // blocks [fbase, fbase + 128) of row qr0 + l32, and `iv` is that row's
+  // normalizer; rows whose bit is clear in `ok` are not written.
+  constexpr int kStgStride = 132;   // floats per staged row (128 + 4 against bank conflicts)
+  static_assert(RG * 32 * kStgStride * 4 <= NS * kTileBytes, "staging fits the tile ring");
+  LDS_AS float* stg = (LDS_AS float*)lds + wave * 32 * kStgStride;
+  auto stage_partial = [&](const f32x16_t* acc, int64_t qr0, int fbase, float iv, uint32_t ok) {
+#pragma unroll
+    for (int f = 0; f < 4; f++)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; a4++) {
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const f32x4_t v = {acc[f][4 * a4] * iv, acc[f][4 * a4 + 1] * iv, acc[f][4 * a4 + 2] * iv,
+                           acc[f][4 * a4 + 3] * iv};
+        *(LDS_AS f32x4_t*)(stg + l32 * kStgStride + 32 * f + 8 * a4 + 4 * h) = v;
+      }
+    // Eight rows at a time: their sixteen LDS reads go out together, so the
+    // read latency is paid once per group rather than once per row.
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += 8) {
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        v[2 * k] = stg[(r0 + k) * kStgStride + lane];
+        v[2 * k + 1] = stg[(r0 + k) * kStgStride + 64 + lane];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        if ((ok >> (r0 + k)) & 1u) {
+          float* w = p.ws + ((qr0 + r0 + k) * p.S + split) * (int64_t)kPartialWidth + fbase;
+          w[lane] = v[2 * k];
+          w[64 + lane] = v[2 * k + 1];
+        }
+      }
+    }
+  };
   auto store_lse = [&]() {
     if (h != 0 || !row_ok) return;
     if (p.S == 1) {
@@ -1455,15 +1495,37 @@ mla_partial_kernel(const PartialParams p) {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int rq = (wave + r) & 3;
-      const int rrow = rb * (32 * RG) + rq * 32 + l32;
-      if (rrow >= p.R) continue;
+      const int rrow0 = rb * (32 * RG) + rq * 32;          // the row block's first row
+      const int rrow = rrow0 + l32;
       const float iv = invbuf[rq * 32 + l32];
+      if (p.S > 1) {
+        const int n_ok = min(32, p.R - rrow0);
+        if (n_ok > 0)
+          stage_partial(&oacc[4 * r], (int64_t)b * p.R + rrow0, 128 * wave, iv,
+                        n_ok >= 32 ? 0xffffffffu : (1u << n_ok) - 1u);
+        continue;
+      }
+      if (rrow >= p.R) continue;
       const int64_t qr = (int64_t)b * p.R + rrow;
 #pragma unroll
       for (int f = 0; f < 4; f++) store_block(qr, 4 * wave + f, oacc[4 * r + f], iv);
     }
     store_lse();
   } else {
+    // Staging pays off for four-wave blocks (128 rows of partials each);
+    // narrower blocks write few rows, and there the extra LDS round trips
+    // cost more latency than the coalescing saves.
+    if (RG == 4 && p.S > 1) {
+      // Every wave is done with the tile ring before any stages into it.
+      __syncthreads();
+      const uint32_t ok = (uint32_t)__builtin_amdgcn_ballot_w64(row_ok);   // lanes 0-31: rows l32
+      const int64_t qr0 = qrow - l32;
+#pragma unroll
+      for (int c = 0; c < 4; c++) stage_partial(&oacc[4 * c], qr0, 128 * c, inv, ok);
+      if (!row_ok) return;
+      store_lse();
+      return;
+    }
     if (!row_ok) return;
 #pragma unroll
     for (int fb = 0; fb < 16; fb++) store_block(qrow, fb, oacc[fb], inv);
