@@ -238,6 +238,20 @@ def test_two_rounds_longest_first(B, H, T, lens, kv_dtype):
     check_full(inp, 2, "two rounds longest first, explicit 2 splits")
 
 
+def test_two_rounds_longest_first_long_fp8_units_sampled_rows():
+    """Two rounds of longest-first pieces whose halves exceed 8192 tokens:
+    the feature-split fp8 step without the residual product."""
+    inp = wl.make_inputs(32, 128, 8, (17000, 21000), kv_dtype="fp8", out_dtype="bf16", seed=64, device=DEV)
+    assert binding.num_kv_splits(32, 8, 128, inp.max_len, 0, True) == 2
+    out, lse, _ = binding.decode(inp)
+    torch.cuda.synchronize()
+    n_total = inp.B * inp.T * inp.H
+    rows = sample_rows(n_total, 64, seed=64)
+    _say("[gpu] two rounds, long fp8 units: oracle on %d rows" % rows.size)
+    ref_o, ref_l = oracle_rows(inp.to("cpu"), rows=rows)
+    compare(out, lse, ref_o, ref_l, "fp8", rows=rows, what="two rounds long fp8 units")
+
+
 def test_host_bound_far_above_the_lengths():
     """max_seq_len four times the longest sequence: the pieces follow the
     actual lengths, not the bound."""
