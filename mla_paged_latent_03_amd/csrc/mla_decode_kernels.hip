@@ -508,6 +508,42 @@ mla_partial_kernel(const PartialParams p) {
   }
   const int n_vis = L - p.T + t_row + 1;  // dense: visible tokens of this row
 
+  // ---- query operand registers.  Dense: filled after the first DMAs are
+  // issued, so that the two latencies overlap.  Sparse: filled first, under
+  // the latency of the index-table loads (the DMAs need the table).
+  constexpr int QREGS = FP8 ? 8 * K::kQkSteps : 4 * K::kQkSteps;
+  int qreg[QREGS];
+  // ---- query operand in registers (B side: lane holds row l32, a K slice)
+  // bf16: step k covers features 16k .. 16k+15; lane half h holds 8 of them.
+  // fp8 : step k covers features 64k .. 64k+63; lane half h holds 32 of them.
+  auto load_q = [&]() __attribute__((always_inline)) {
+    // Rows past the end read row 0 of the sequence (always present) and are zeroed.
+    const int64_t qsafe = row_ok ? qrow : (int64_t)b * p.R;
+    const uint8_t* qn = p.q_nope + qsafe * (512 * (FP8 ? 1 : 2));
+    const uint8_t* qp = p.q_pe + qsafe * (64 * (FP8 ? 1 : 2));
+    const int keep = row_ok ? -1 : 0;
+    if (FP8) {
+#pragma unroll
+      for (int k = 0; k < K::kQkSteps; k++) {
+        const uint8_t* src = k < 8 ? qn + 64 * k + 32 * h : qp + 32 * h;
+        const i32x4_t a = *(const i32x4_t*)src;
+        const i32x4_t c = *(const i32x4_t*)(src + 16);
+#pragma unroll
+        for (int i = 0; i < 4; i++) { qreg[8 * k + i] = a[i] & keep; qreg[8 * k + 4 + i] = c[i] & keep; }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < K::kQkSteps; k++) {
+        const uint8_t* src = k < 32 ? qn + 2 * (16 * k + 8 * h) : qp + 2 * (16 * (k - 32) + 8 * h);
+        const i32x4_t a = *(const i32x4_t*)src;
+#pragma unroll
+        for (int i = 0; i < 4; i++) qreg[4 * k + i] = a[i] & keep;
+      }
+    }
+  };
+
+  if constexpr (SPARSE) load_q();
+
   // ---- unit table in LDS.  Dense: physical page of each page of the unit
   // (-1 if out of range).  Sparse: address of each index's token row, or of
   // the zero row for padding / out-of-range entries.
@@ -515,16 +551,29 @@ mla_partial_kernel(const PartialParams p) {
   if (SPARSE) {
     const int32_t* idx = p.topk + ((int64_t)b * p.T + (rb / p.n_hb)) * p.K + idx_begin;
     const int n_ent = n_tiles * K::kTileTok;
-    for (int e = threadIdx.x; e < n_ent; e += 64 * RG) {
-      uint64_t a = zero_row;
-      if (e < idx_count) {
-        const int j = idx[e];
-        if (j >= 0 && j < L) {
-          const int pg = p.block_table[(int64_t)b * p.MB + (j >> 6)];
-          if (pg >= 0 && pg < p.NB) a = (uint64_t)(uintptr_t)(p.kv + ((int64_t)pg * 64 + (j & 63)) * K::kRowBytes);
-        }
-      }
-      table64[e] = a;
+    // A thread's entries (at most kTableCap / (64 RG)): every index load is
+    // issued before any is used, then every block-table load, so the two
+    // dependent latencies are paid once, not once per entry.
+    constexpr int EPT = (kTableCap + 64 * RG - 1) / (64 * RG);
+    int jv[EPT], pgv[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; k++) {
+      const int e = threadIdx.x + k * 64 * RG;
+      jv[k] = e < idx_count ? idx[e] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; k++) {
+      const int j = jv[k];
+      pgv[k] = (j >= 0 && j < L) ? p.block_table[(int64_t)b * p.MB + (j >> 6)] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; k++) {
+      const int e = threadIdx.x + k * 64 * RG;
+      const int j = jv[k], pg = pgv[k];
+      const uint64_t a = (j >= 0 && j < L && pg >= 0 && pg < p.NB)
+                             ? (uint64_t)(uintptr_t)(p.kv + ((int64_t)pg * 64 + (j & 63)) * K::kRowBytes)
+                             : zero_row;
+      if (e < n_ent) table64[e] = a;
     }
     if (threadIdx.x < K::kTileTok) table64[kTableCap + threadIdx.x] = zero_row;
   } else {
@@ -536,9 +585,6 @@ mla_partial_kernel(const PartialParams p) {
   }
   __syncthreads();
 
-  // ---- query operand registers (filled after the first DMAs are issued)
-  constexpr int QREGS = FP8 ? 8 * K::kQkSteps : 4 * K::kQkSteps;
-  int qreg[QREGS];
 
   // ---- DMA source offsets.  Wave w fills tile units [w*NI*64, (w+1)*NI*64):
   // instruction j writes LDS units pos = (w*NI + j)*64 + lane, i.e. token
@@ -616,34 +662,7 @@ mla_partial_kernel(const PartialParams p) {
   };
   issue_first_tiles();
 
-  // ---- query operand in registers (B side: lane holds row l32, a K slice)
-  // bf16: step k covers features 16k .. 16k+15; lane half h holds 8 of them.
-  // fp8 : step k covers features 64k .. 64k+63; lane half h holds 32 of them.
-  {
-    // Rows past the end read row 0 of the sequence (always present) and are zeroed.
-    const int64_t qsafe = row_ok ? qrow : (int64_t)b * p.R;
-    const uint8_t* qn = p.q_nope + qsafe * (512 * (FP8 ? 1 : 2));
-    const uint8_t* qp = p.q_pe + qsafe * (64 * (FP8 ? 1 : 2));
-    const int keep = row_ok ? -1 : 0;
-    if (FP8) {
-#pragma unroll
-      for (int k = 0; k < K::kQkSteps; k++) {
-        const uint8_t* src = k < 8 ? qn + 64 * k + 32 * h : qp + 32 * h;
-        const i32x4_t a = *(const i32x4_t*)src;
-        const i32x4_t c = *(const i32x4_t*)(src + 16);
-#pragma unroll
-        for (int i = 0; i < 4; i++) { qreg[8 * k + i] = a[i] & keep; qreg[8 * k + 4 + i] = c[i] & keep; }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < K::kQkSteps; k++) {
-        const uint8_t* src = k < 32 ? qn + 2 * (16 * k + 8 * h) : qp + 2 * (16 * (k - 32) + 8 * h);
-        const i32x4_t a = *(const i32x4_t*)src;
-#pragma unroll
-        for (int i = 0; i < 4; i++) qreg[4 * k + i] = a[i] & keep;
-      }
-    }
-  }
+  if constexpr (!SPARSE) load_q();
 
   // ---- per-lane LDS read offsets (within a tile)
   // QK operand A = K tile rows: token 32*tb + l32, unit(s) for step k.
