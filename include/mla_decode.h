@@ -46,7 +46,9 @@
  * ceil(longest / splits) pages.  A long
  * sequence of a mixed batch thus gets more pieces than a short one, and all
  * pieces are about equally long.  Slots past a sequence's k-th get lse =
- * -inf and no outputs.  Other calls cut fixed chunks of
+ * -inf and no outputs.  The two-round plan of mla_num_kv_splits (two
+ * splits, batch of one to two rounds of pieces) cuts the same way for two
+ * rounds and numbers the pieces longest first.  Other calls cut fixed chunks of
  * ceil(ceil(max_seq_len / 64) / splits) pages.  Either way the merged result
  * is the same attention; rounding differs with the cut.
  *
@@ -126,8 +128,11 @@ const char* mla_status_string(mla_status_t status);
  * units occupy the chip's workgroup slots; the cheapest wins.  A dense call
  * whose pieces are cut by the actual lengths (see Split-KV above) then gets
  * twice that many slots (at most one per page), so that long sequences of a
- * mixed batch can take more pieces.  Passing the returned count explicitly
- * gives the same launch.  Deterministic in its arguments; topk = 0 means a
+ * mixed batch can take more pieces.  A dense call that the costing gives one
+ * split, with at least four row blocks per sequence and a batch that fills
+ * one round of workgroup slots but not two (at most 64 sequences), gets 2:
+ * its sequences are cut into pieces for two rounds, dispatched longest piece
+ * first.  Passing the returned count explicitly gives the same launch.  Deterministic in its arguments; topk = 0 means a
  * dense call, otherwise a sparse call with that K.  Returns 0 on invalid
  * arguments.
  */
