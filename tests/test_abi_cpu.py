@@ -99,8 +99,11 @@ def test_launch_waves_follow_the_row_block_rules(lib):
     assert binding.launch_waves(32, 8, 128, 32768, 0, False) == 4
     assert binding.launch_waves(256, 1, 128, 300, 0, False) == 4
     assert binding.launch_waves(64, 1, 128, 65536, 2048, False) == 4
-    # 16 rows per sequence fit one wave.
-    assert binding.launch_waves(128, 1, 16, 8192, 0, False) == 1
+    # 16 rows per sequence: a dense call still takes two waves (the second has
+    # no rows but shares each tile's DMA); a sparse one takes one.
+    assert binding.launch_waves(128, 1, 16, 8192, 0, False) == 2
+    assert binding.launch_waves(128, 1, 16, 8192, 0, True) == 2
+    assert binding.launch_waves(128, 1, 16, 65536, 2048, False) == 1
     # Few short sequences: narrower row blocks (and splits) fill more of the chip.
     assert binding.launch_waves(4, 1, 64, 300, 0, False) == 1
     # 64 rows and units enough for two workgroups per compute unit: two waves.

@@ -64,7 +64,7 @@ def test_tiny_workload_split_results_agree():
 @pytest.mark.parametrize("H,T,lens,splits", [
     (16, 1, [1, 63, 64, 65, 700], 0),         # one-token, page-edge and ragged tails
     (16, 1, [1, 63, 64, 65, 700], 3),
-    (32, 1, [129, 2000], 0),                  # one 32-row wave
+    (32, 1, [129, 2000], 0),                  # 32 rows: a two-wave block whose second wave is empty
     (16, 4, [3, 4, 5, 130, 1000], 0),         # MTP: first queries of short sequences see nothing
     (16, 4, [3, 4, 5, 130, 1000], 2),
     (64, 2, [77, 1500], 2),                   # two waves per workgroup
@@ -394,8 +394,8 @@ def _plant_large_logit(inp, pos):
 
 
 @pytest.mark.parametrize("kind,B,H,T,waves", [
-    ("bf16", 256, 32, 4, 4), ("bf16", 256, 128, 1, 4), ("bf16", 4, 16, 1, 1), ("bf16", 512, 64, 1, 2),
-    ("fp8", 256, 32, 4, 4), ("fp8", 4, 16, 1, 1),
+    ("bf16", 256, 32, 4, 4), ("bf16", 256, 128, 1, 4), ("bf16", 4, 64, 1, 1), ("bf16", 512, 64, 1, 2),
+    ("bf16", 4, 16, 1, 2), ("fp8", 256, 32, 4, 4), ("fp8", 4, 64, 1, 1), ("fp8", 4, 16, 1, 2),
     ("sparse", 256, 128, 1, 4), ("sparse", 4, 16, 1, 1),
     ("sparse_fp8", 256, 128, 1, 4), ("sparse_fp8", 4, 16, 1, 1),
 ])
