@@ -131,6 +131,13 @@ __device__ inline float max_across_halves(float x) { return fmaxf(x, other_half(
 __device__ inline float sum_across_halves(float x) { return x + other_half(x); }
 
 // 16-byte global -> LDS DMA: lane i writes LDS bytes [m0 + 16 i, m0 + 16 i + 16).
+// Both DMA helpers load with the non-temporal hint (nt): cache lines are
+// streamed, so they do not push out what is reused (query rows, tables,
+// partials).  Each workgroup reads its tiles once, and row blocks sharing a
+// piece run side by side.  Measured against the same kernels without the
+// hint (alternating calls on one GPU): R1-shaped batch 143.9 -> 129.2 us,
+// MTP-3 fp8 716 -> 704 us, sparse bf16 77.5 -> 71.4 us, sparse fp8 61.7 ->
+// 57.5 us, MTP-7 unchanged.
 // Issued from inline asm so the compiler does not treat it as an LDS store
 // (it would otherwise drain every in-flight DMA before each LDS read it
 // cannot prove disjoint); completion is tracked explicitly with vmcnt.
@@ -142,7 +149,7 @@ __device__ inline float sum_across_halves(float x) { return x + other_half(x); }
 // SGPR; buffer_rsrc() provides those once per descriptor.  The build scans
 // the compiled kernels for both cases (asm_hazards.py).
 __device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_byte_addr) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gsrc), "{m0}"(lds_byte_addr) : "memory");
 }
 
 // 16-byte buffer -> LDS DMA: lane i reads rsrc.base + voff_i + soff and
@@ -151,7 +158,7 @@ __device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
 // tokens of a tile become zero vectors.  Inline asm for the same reason as
 // dma16().
 __device__ inline void dma16_buf(int voff, i32x4_t rsrc, int soff, uint32_t lds_byte_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(rsrc), "s"(soff),
                "{m0}"(lds_byte_addr)
                : "memory");
 }
