@@ -238,6 +238,22 @@ def test_two_rounds_longest_first(B, H, T, lens, kv_dtype):
     check_full(inp, 2, "two rounds longest first, explicit 2 splits")
 
 
+def test_two_rounds_longest_first_largest_batch():
+    """63 sequences with eight row blocks each: one short of two full rounds."""
+    inp = wl.make_inputs(63, 128, 8, (1, 300), kv_dtype="bf16", out_dtype="f32", seed=65, poison=True)
+    assert binding.num_kv_splits(63, 8, 128, inp.max_len, 0, False) == 2
+    check_full(inp, 0, "two rounds, 63 sequences")
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_feature_split_rows_not_a_multiple_of_128(splits):
+    """The feature-split fp8 step with 80 rows (row blocks 2 and 3 partly or
+    wholly empty), written directly and as staged partials."""
+    inp = wl.make_inputs(2, 40, 2, [20000, 17000], kv_dtype="fp8", out_dtype="f32", seed=66, poison=True)
+    assert binding.launch_waves(2, 2, 40, inp.max_len, 0, True) == 4
+    check_full(inp, splits, "feature split, 80 rows, %d split(s)" % splits)
+
+
 def test_two_rounds_longest_first_long_fp8_units_sampled_rows():
     """Two rounds of longest-first pieces whose halves exceed 8192 tokens:
     the feature-split fp8 step without the residual product."""
