@@ -1359,11 +1359,11 @@ mla_partial_kernel(const PartialParams p) {
       }
     } else {
       // Two-slot loop (one or two waves): tile i+1 streams into the other
-      // slot while tile i is computed, its DMA instructions spread between
-      // the QK products (a wave can keep at most 63 vector-memory
-      // instructions in flight, so a one-wave workgroup holds one tile in
-      // flight at a time).  Past the end the slot gets a zero fill, which
-      // keeps the wait a constant.
+      // slot while tile i is computed; its DMA instructions go out right
+      // after the first QK product (a wave can keep at most 63
+      // vector-memory instructions in flight, so a one-wave workgroup holds
+      // one tile in flight at a time).  Past the end the slot gets a zero
+      // fill, which keeps the wait a constant.
       static_assert(NS == 2, "two-slot loop");
       if (pass > 0) issue_first_tiles();
       for (int i = 0; i < n_tiles; i++) {
@@ -1381,10 +1381,14 @@ mla_partial_kernel(const PartialParams p) {
             if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(tile, n + 2);
             __builtin_amdgcn_sched_barrier(0);
             qk_mfma(sacc, n, qa[n % 3]);
-            // DMA instructions j with floor(j * NQK / NI) == n follow product n.
+            // All of the next tile's DMA instructions follow the first
+            // product, so its data has the whole tile's compute to arrive
+            // (R1-shaped batch: 130.6 -> 124.1 us per call against spreading
+            // them over the QK products, alternating on one GPU).
+            if (n == 0) {
 #pragma unroll
-            for (int j = (n * NI + NQK - 1) / NQK; j < ((n + 1) * NI + NQK - 1) / NQK; j++)
-              dma_issue(src, (i + 1) % NS, j);
+              for (int j = 0; j < NI; j++) dma_issue(src, (i + 1) % NS, j);
+            }
             __builtin_amdgcn_sched_barrier(0);
           }
           drain_scores(sacc);
