@@ -245,7 +245,18 @@ mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv
   hipStream_t st = (hipStream_t)stream;
   const int64_t unit_tokens = (int64_t)(sparse ? pl.chunk : pl.unit_pages * MLA_BLOCK_SIZE);
   const bool resid = fp8 && unit_tokens <= mla::kFp8ResidualMaxUnitTokens;
-  if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, resid, grid, st) != hipSuccess) return MLA_ERR_HIP;
+  if (fp8 && !sparse && !resid) {
+    // Planned for long units, but a sequence shorter than the others still
+    // makes a short one: the residual-product kernel takes those, over the
+    // same grid, and each launch leaves the other's units alone.
+    p.unit_filter = 1;
+    if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, false, grid, st) != hipSuccess) return MLA_ERR_HIP;
+    p.unit_filter = 2;
+    if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, true, grid, st) != hipSuccess) return MLA_ERR_HIP;
+  } else {
+    p.unit_filter = 0;
+    if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, resid, grid, st) != hipSuccess) return MLA_ERR_HIP;
+  }
   if (pl.S > 1 && !stage1_only) {
     mla::MergeParams m{};
     m.ws = (const float*)workspace;

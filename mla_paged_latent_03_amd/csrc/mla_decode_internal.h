@@ -31,6 +31,7 @@ struct PartialParams {
   int balance;                  // dense, S > 1: length-balanced pieces instead of fixed chunks
   int n_target;                 // balanced: pieces the batch may be cut into (one round of workgroups)
   int lpt;                      // balanced, B <= 64: number pieces longest first (two rounds)
+  int unit_filter;              // dense fp8: 0 every unit; 1 units longer than kFp8ResidualMaxUnitTokens; 2 the others
   int max_pages;                // balanced: pages of max_seq_len (longer sequences are cut there)
   float qk_scale;               // softmax_scale * log2(e) [* q_scale * kv_scale]
   float out_scale;              // kv_scale (fp8) or 1

@@ -512,6 +512,16 @@ mla_partial_kernel(const PartialParams p) {
     const int tok_end = n_unit_pages > 0 ? min(p1 * 64, L) : tok_begin;
     n_tiles = (tok_end - tok_begin + K::kTileTok - 1) / K::kTileTok;
     if (n_tiles < 0) n_tiles = 0;
+    // fp8 calls planned for long units run in two launches over the same
+    // grid: this one takes the units of its own length class and leaves
+    // the others (workgroup-uniform, before any memory traffic).  Units of
+    // at most kFp8ResidualMaxUnitTokens tokens go to the launch with the
+    // residual product, so that a short sequence in a batch of long ones
+    // keeps its weights to about 2^-8.
+    if (p.unit_filter != 0) {
+      const bool is_short = tok_end - tok_begin <= kFp8ResidualMaxUnitTokens;
+      if (is_short != (p.unit_filter == 2)) return;
+    }
   }
   const int n_vis = L - p.T + t_row + 1;  // dense: visible tokens of this row
 

@@ -186,6 +186,30 @@ def test_fp8_long_units_without_residual_product():
     compare(out, lse, ref_o, ref_l, "fp8", rows=rows, what="fp8 long units")
 
 
+@pytest.mark.parametrize("lens,splits", [([300, 9000, 20000, 1], 1), ([20000] * 7 + [300], 2)])
+def test_fp8_short_sequence_among_long_units(lens, splits):
+    """A call planned for long fp8 units (no residual product) with a short
+    sequence in the batch: the short units go to the residual-product launch,
+    so their rows keep the fp8 tolerance."""
+    inp = wl.make_inputs(len(lens), 32, 4, lens, kv_dtype="fp8", out_dtype="f32", seed=95, poison=True)
+    check_full(inp, splits, "fp8 short among long, splits=%d" % splits)
+
+
+def test_fp8_short_sequence_in_the_long_unit_workload_sampled_rows():
+    """The 80k-token MTP-3 shape with its last sequence 300 tokens long, in the
+    library's own launch plan: every row of the short sequence and a sample of
+    the others."""
+    lens = [80000] * 63 + [300]
+    inp = wl.make_inputs(64, 32, 4, lens, kv_dtype="fp8", out_dtype="bf16", seed=96, device=DEV)
+    out, lse, _ = binding.decode(inp)
+    torch.cuda.synchronize()
+    R = inp.T * inp.H
+    rows = np.unique(np.concatenate([np.arange(63 * R, 64 * R), sample_rows(63 * R, 40, seed=96)]))
+    _say("[gpu] short among 80k-token sequences: oracle on %d rows" % rows.size)
+    ref_o, ref_l = oracle_rows(inp.to("cpu"), rows=rows)
+    compare(out, lse, ref_o, ref_l, "fp8", rows=rows, what="fp8 short among 80k-token sequences")
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 def test_sequence_past_the_split_cap_is_split(kv_dtype):
     """One split covers at most 1024 pages: a 70000-token sequence needs two,
