@@ -51,7 +51,10 @@ struct MergeParams {
 };
 
 // fp8 work units of at most this many tokens use the residual product.
-constexpr int kFp8ResidualMaxUnitTokens = 8192;
+// (Without it, units a little over 8192 tokens measured row errors up to 0.025
+// against the oracle on N(0,1) data, close to the 3e-2 bound; from about
+// 16000 tokens on, 0.006.)
+constexpr int kFp8ResidualMaxUnitTokens = 16384;
 
 hipError_t launch_partial_kernel(const PartialParams& p, bool fp8, bool sparse, int rg, bool resid, int grid,
                                  hipStream_t stream);

@@ -183,13 +183,17 @@ __device__ inline i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
 // callers end a chain with mfma_drain(acc) before any VALU reads the result
 // (an XDL result needs about 18).  Back-to-back products on one accumulator
 // need no padding (the compiler emits none for such chains either).
-__device__ inline void mfma_f8_first(f32x16_t& acc, const i32x8_t& a, const i32x8_t& b, int sa, int sb) {
-  asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
-               : "=&v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
-}
 __device__ inline void mfma_f8_acc(f32x16_t& acc, const i32x8_t& a, const i32x8_t& b, int sa, int sb) {
   asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
                : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+// The same fp8 product without block scales (both 2^0), for the QK chain:
+// one 8-byte instruction instead of the 16-byte scaled form.
+__device__ inline void mfma_f8_first_plain(f32x16_t& acc, const i32x8_t& a, const i32x8_t& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_f8_acc_plain(f32x16_t& acc, const i32x8_t& a, const i32x8_t& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_bf16_first(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
@@ -790,8 +794,8 @@ mla_partial_kernel(const PartialParams p) {
       const int k = n % K::kQkSteps, tb = n / K::kQkSteps;   // token block 0's chain first
       const i32x8_t bq = {qreg[8 * k], qreg[8 * k + 1], qreg[8 * k + 2], qreg[8 * k + 3],
                           qreg[8 * k + 4], qreg[8 * k + 5], qreg[8 * k + 6], qreg[8 * k + 7]};
-      if (k == 0) mfma_f8_first(sacc[tb], a, bq, e8m0_one, e8m0_one);
-      else mfma_f8_acc(sacc[tb], a, bq, e8m0_one, e8m0_one);
+      if (k == 0) mfma_f8_first_plain(sacc[tb], a, bq);
+      else mfma_f8_acc_plain(sacc[tb], a, bq);
     } else {
       const i32x4_t bq = {qreg[4 * n], qreg[4 * n + 1], qreg[4 * n + 2], qreg[4 * n + 3]};
       if (n == 0) mfma_bf16_first(sacc[0], a, __builtin_bit_cast(bf16x8_t, bq));

@@ -175,10 +175,10 @@ def test_fp8_scales_are_read_every_call():
 # ------------------------------------------------------------------ edge and limit cases
 
 def test_fp8_long_units_without_residual_product():
-    """Units longer than 8192 tokens use one fp8 PV product per block (no
+    """Units longer than 16384 tokens use one fp8 PV product per block (no
     residual); with 128 rows per sequence and many sequences they run on the
     four-wave feature-split kernel."""
-    inp = wl.make_inputs(64, 32, 4, (8500, 9500), kv_dtype="fp8", out_dtype="f32", seed=51)
+    inp = wl.make_inputs(64, 32, 4, (17000, 19000), kv_dtype="fp8", out_dtype="f32", seed=51)
     assert binding.launch_waves(64, 4, 32, inp.max_len, 0, True) == 4
     out, lse = run_case(inp, 1, "fp8 long units, one split")
     rows = sample_rows(64 * 4 * 32, 96, seed=51)
@@ -186,7 +186,7 @@ def test_fp8_long_units_without_residual_product():
     compare(out, lse, ref_o, ref_l, "fp8", rows=rows, what="fp8 long units")
 
 
-@pytest.mark.parametrize("lens,splits", [([300, 9000, 20000, 1], 1), ([20000] * 7 + [300], 2)])
+@pytest.mark.parametrize("lens,splits", [([300, 9000, 20000, 1], 1), ([40000] * 3 + [300], 2)])
 def test_fp8_short_sequence_among_long_units(lens, splits):
     """A call planned for long fp8 units (no residual product) with a short
     sequence in the batch: the short units go to the residual-product launch,
@@ -273,15 +273,15 @@ def test_two_rounds_longest_first_largest_batch():
 def test_feature_split_rows_not_a_multiple_of_128(splits):
     """The feature-split fp8 step with 80 rows (row blocks 2 and 3 partly or
     wholly empty), written directly and as staged partials."""
-    inp = wl.make_inputs(2, 40, 2, [20000, 17000], kv_dtype="fp8", out_dtype="f32", seed=66, poison=True)
+    inp = wl.make_inputs(2, 40, 2, [40000, 34000], kv_dtype="fp8", out_dtype="f32", seed=66, poison=True)
     assert binding.launch_waves(2, 2, 40, inp.max_len, 0, True) == 4
     check_full(inp, splits, "feature split, 80 rows, %d split(s)" % splits)
 
 
 def test_two_rounds_longest_first_long_fp8_units_sampled_rows():
-    """Two rounds of longest-first pieces whose halves exceed 8192 tokens:
+    """Two rounds of longest-first pieces whose halves exceed 16384 tokens:
     the feature-split fp8 step without the residual product."""
-    inp = wl.make_inputs(32, 128, 8, (17000, 21000), kv_dtype="fp8", out_dtype="bf16", seed=64, device=DEV)
+    inp = wl.make_inputs(32, 128, 8, (34000, 40000), kv_dtype="fp8", out_dtype="bf16", seed=64, device=DEV)
     assert binding.num_kv_splits(32, 8, 128, inp.max_len, 0, True) == 2
     out, lse, _ = binding.decode(inp)
     torch.cuda.synchronize()
