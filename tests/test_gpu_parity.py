@@ -457,9 +457,13 @@ def test_large_logit_jump_reruns_against_exact_maximum(kind, B, H, T, waves):
 
 # ------------------------------------------------------------------ graph capture
 
-def test_hip_graph_replay_matches_eager():
-    inp = wl.make_inputs(4, 32, 4, [100, 800, 2000, 64], kv_dtype="fp8", out_dtype="bf16", seed=17).to(DEV)
-    _say("[gpu] graph capture")
+@pytest.mark.parametrize("lens", [[100, 800, 2000, 64], [40000, 300, 20000, 1]])
+def test_hip_graph_replay_matches_eager(lens):
+    """Short units (one launch with the residual product), and long units
+    next to short ones (the long-unit and residual launches), then the merge,
+    all captured in one graph."""
+    inp = wl.make_inputs(4, 32, 4, lens, kv_dtype="fp8", out_dtype="bf16", seed=17).to(DEV)
+    _say("[gpu] graph capture, lengths %s" % lens)
     eager_o, eager_l, ws = binding.decode(inp, num_kv_splits=3)
     torch.cuda.synchronize()
     out = torch.empty_like(eager_o)
