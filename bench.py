@@ -135,8 +135,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build's hot path has no multi-GPU form "
-              "(the sequence-sharded design is described, not built). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: this decode library runs on a single GPU "
+              "(its sequence-sharded multi-GPU form is not implemented). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
