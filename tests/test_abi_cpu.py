@@ -221,3 +221,9 @@ def test_asm_hazard_scan_flags_m0_and_sgpr_hazards():
     assert hz.scan(compiler_owned) == []
     sparse = _asm("s_add_i32 m0, s37, 0x400", ";;#ASMSTART", "global_load_lds_dwordx4 v[2:3], off", ";;#ASMEND")
     assert len(hz.scan(sparse)) == 1
+    # The forms the kernels issue carry the non-temporal hint; the scan must still see them.
+    nt_dense = _asm("s_mov_b32 m0, s1", ";;#ASMSTART", "buffer_load_dwordx4 v1, s[8:11], s12 offen nt lds", ";;#ASMEND")
+    assert len(hz.scan(nt_dense)) == 1
+    nt_sparse = _asm("s_add_i32 m0, s37, 0x400", ";;#ASMSTART", "global_load_lds_dwordx4 v[2:3], off nt",
+                     ";;#ASMEND")
+    assert len(hz.scan(nt_sparse)) == 1
