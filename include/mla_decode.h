@@ -196,7 +196,12 @@ mla_status_t mla_decode(const void* q_nope, const void* q_pe, const void* kv_cac
  * dequantized latent average, i.e. it carries kv_scale.  Inside, both
  * products run on fp8 MFMA; the softmax probabilities are scaled by 2^8
  * before their e4m3 rounding so they stay in the format's normal range.
- * Other arguments as mla_decode; workspace sized with kv_fp8 = 1.
+ * Work units of at most 16384 tokens also multiply V by the e4m3 residual
+ * of the probabilities (about 2^-8 per weight).  When the plan expects
+ * longer units, the call enqueues two first-stage kernels over the same
+ * grid, one per unit-length class, so a short sequence in such a batch
+ * still gets the residual product.  Other arguments as mla_decode;
+ * workspace sized with kv_fp8 = 1.
  */
 mla_status_t mla_decode_fp8(const void* q_nope, const void* q_pe, const void* kv_cache,
                             const int32_t* block_table, const int32_t* seq_lens, int batch,
