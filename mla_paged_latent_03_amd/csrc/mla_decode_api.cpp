@@ -85,10 +85,11 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
   if (s_max < 1) s_max = 1;
 
   // Dense blocks of at most 32 rows start from two waves: the second wave
-  // has no rows, but it takes half of each tile's DMA instructions, and a
-  // one-wave block waits longer for its tiles (R1-shaped batch, 16 rows per
-  // sequence: 149.6 against 153.6 us per call, alternating on one GPU).  One
-  // wave is costed the same and so never replaces it there.
+  // has no rows, but it takes half of each tile's DMA instructions (R1-shaped
+  // batch, B=128 with 16 rows per sequence: 149.6 against 153.6 us per call
+  // with the DMA spread over the QK products; with the DMA issued in one
+  // burst, as now, the two widths measure the same).  One wave is costed the
+  // same and so never replaces it there.
   const int g_first = std::max(rg_for_rows(rows_blk), (!sparse && rows_blk <= 32) ? 2 : 1);
   int rg = g_first, S = 1;
   double best = -1.0;
