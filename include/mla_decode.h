@@ -196,11 +196,14 @@ mla_status_t mla_decode(const void* q_nope, const void* q_pe, const void* kv_cac
  * dequantized latent average, i.e. it carries kv_scale.  Inside, both
  * products run on fp8 MFMA; the softmax probabilities are scaled by 2^8
  * before their e4m3 rounding so they stay in the format's normal range.
- * Work units of at most 16384 tokens also multiply V by the e4m3 residual
- * of the probabilities (about 2^-8 per weight).  When the plan expects
- * longer units, the call enqueues two first-stage kernels over the same
- * grid, one per unit-length class, so a short sequence in such a batch
- * still gets the residual product.  Other arguments as mla_decode;
+ * Work units planned at most 16384 tokens long also multiply V by the e4m3
+ * residual of the probabilities (about 2^-8 per weight).  Longer units
+ * skip that product while their weight is spread over many tokens: a row
+ * whose bound of sum w^2 (w its normalized weights) exceeds 2^-7 gets the
+ * residual product of its heaviest 64-token tile added, or, when that tile
+ * alone does not bring it under the bound, its unit reruns with the
+ * residual product throughout.  One launch per stage either way.  Other
+ * arguments as mla_decode;
  * workspace sized with kv_fp8 = 1.
  */
 mla_status_t mla_decode_fp8(const void* q_nope, const void* q_pe, const void* kv_cache,

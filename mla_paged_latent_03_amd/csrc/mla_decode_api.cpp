@@ -244,20 +244,13 @@ mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv
   p.ws = pl.S > 1 ? (float*)workspace : nullptr;
   const int grid = (int)((units + 7) / 8 * 8);
   hipStream_t st = (hipStream_t)stream;
+  // fp8: units planned at most kFp8ResidualMaxUnitTokens long take the
+  // residual-product kernel.  The others run without it and rerun a unit
+  // with it when a few tokens carry most of a row's weight (a short
+  // sequence in a batch of long ones, or a peaked softmax).
   const int64_t unit_tokens = (int64_t)(sparse ? pl.chunk : pl.unit_pages * MLA_BLOCK_SIZE);
   const bool resid = fp8 && unit_tokens <= mla::kFp8ResidualMaxUnitTokens;
-  if (fp8 && !sparse && !resid) {
-    // Planned for long units, but a sequence shorter than the others still
-    // makes a short one: the residual-product kernel takes those, over the
-    // same grid, and each launch leaves the other's units alone.
-    p.unit_filter = 1;
-    if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, false, grid, st) != hipSuccess) return MLA_ERR_HIP;
-    p.unit_filter = 2;
-    if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, true, grid, st) != hipSuccess) return MLA_ERR_HIP;
-  } else {
-    p.unit_filter = 0;
-    if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, resid, grid, st) != hipSuccess) return MLA_ERR_HIP;
-  }
+  if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, resid, grid, st) != hipSuccess) return MLA_ERR_HIP;
   if (pl.S > 1 && !stage1_only) {
     mla::MergeParams m{};
     m.ws = (const float*)workspace;

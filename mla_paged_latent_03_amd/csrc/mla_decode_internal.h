@@ -31,7 +31,6 @@ struct PartialParams {
   int balance;                  // dense, S > 1: length-balanced pieces instead of fixed chunks
   int n_target;                 // balanced: pieces the batch may be cut into (one round of workgroups)
   int lpt;                      // balanced, B <= 64: number pieces longest first (two rounds)
-  int unit_filter;              // dense fp8: 0 every unit; 1 units longer than kFp8ResidualMaxUnitTokens; 2 the others
   int max_pages;                // balanced: pages of max_seq_len (longer sequences are cut there)
   float qk_scale;               // softmax_scale * log2(e) [* q_scale * kv_scale]
   float out_scale;              // kv_scale (fp8) or 1
@@ -50,10 +49,11 @@ struct MergeParams {
   float* lse;
 };
 
-// fp8 work units of at most this many tokens use the residual product.
-// (Without it, units a little over 8192 tokens measured row errors up to 0.025
-// against the oracle on N(0,1) data, close to the 3e-2 bound; from about
-// 16000 tokens on, 0.006.)
+// fp8 work units planned at most this many tokens long use the residual
+// product from the start.  (Without it, units a little over 8192 tokens
+// measured row errors up to 0.025 against the oracle on N(0,1) data, close
+// to the 3e-2 bound; from about 16000 tokens on, 0.006.)  Longer units run
+// without it and rerun a unit with it when its weights need it.
 constexpr int kFp8ResidualMaxUnitTokens = 16384;
 
 hipError_t launch_partial_kernel(const PartialParams& p, bool fp8, bool sparse, int rg, bool resid, int grid,

@@ -60,6 +60,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 #define CONST_AS __attribute__((address_space(4)))
 
 constexpr float kLn2 = 0.6931471805599453f;
+// fp8 without the residual product: a unit is rerun with it when some row's
+// bound of sum_j w_j^2 (w the normalized softmax weights) exceeds this.
+constexpr float kFp8RedoSumSq = 0x1p-7f;
 constexpr float kNegBig = -1.0e30f;  // running-max sentinel: finite, below any logit
 constexpr int kE4m3OnesX4 = 0x38383838;  // four e4m3 1.0 bytes
 
@@ -414,7 +417,10 @@ __device__ __attribute__((always_inline)) inline bool balanced_piece(const Parti
 //   RESID  : fp8 only - also multiply V by the e4m3 rounding residual of P
 //            (a second fp8 product), so each softmax weight is carried to
 //            about 2^-8 instead of 2^-4; chosen for short work units, where
-//            a few tokens can dominate a row
+//            a few tokens can dominate a row.  Without it, a row whose
+//            weight concentrates on a few tokens gets the residual product
+//            of its heaviest tile added afterwards, or its unit reruns with
+//            the residual product (see "the passes" below)
 //
 // With four waves (RG = 4) the tile loop is software-pipelined: the QK
 // products of tile i+1 are issued interleaved with the PV products of tile
@@ -436,15 +442,19 @@ mla_partial_kernel(const PartialParams p) {
   constexpr int kTableBytes = SPARSE ? (kTableCap + K::kTileTok) * 8 : kTableCap * 4;
   constexpr int kPBytes = FS ? 4 * 2048 : 0;      // FS: P tile of each row block (64 lanes x 32 B)
   constexpr int kScBytes = FS ? 4 * 64 * 4 : 0;   // FS: E8M0 scales of each row block (per lane)
+  constexpr bool kFixTiles = FP8 && !SPARSE && !RESID;   // pass 0 without the residual product
+  constexpr int kFixWords = kFixTiles ? kDensePagesMax / 32 : 0;   // bitmap of tiles to fix (one page each)
 
   // LDS: [ring of NS tiles][unit table: int32 x kTableCap][FS: P tiles][FS: scales][redo flag]
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kTileBytes + kTableBytes + kPBytes + kScBytes + 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kTileBytes + kTableBytes + kPBytes + kScBytes + 16 +
+                                                         4 * kFixWords];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
   LDS_AS int* table = (LDS_AS int*)(lds + NS * kTileBytes);
   LDS_AS uint64_t* table64 = (LDS_AS uint64_t*)(lds + NS * kTileBytes);
   LDS_AS uint8_t* pbuf = lds + NS * kTileBytes + kTableBytes;
   LDS_AS int* scbuf = (LDS_AS int*)(pbuf + kPBytes);
   LDS_AS int* redo_flag = (LDS_AS int*)(pbuf + kPBytes + kScBytes);
+  LDS_AS uint32_t* fix_map = (LDS_AS uint32_t*)(pbuf + kPBytes + kScBytes + 16);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -516,16 +526,6 @@ mla_partial_kernel(const PartialParams p) {
     const int tok_end = n_unit_pages > 0 ? min(p1 * 64, L) : tok_begin;
     n_tiles = (tok_end - tok_begin + K::kTileTok - 1) / K::kTileTok;
     if (n_tiles < 0) n_tiles = 0;
-    // fp8 calls planned for long units run in two launches over the same
-    // grid: this one takes the units of its own length class and leaves
-    // the others (workgroup-uniform, before any memory traffic).  Units of
-    // at most kFp8ResidualMaxUnitTokens tokens go to the launch with the
-    // residual product, so that a short sequence in a batch of long ones
-    // keeps its weights to about 2^-8.
-    if (p.unit_filter != 0) {
-      const bool is_short = tok_end - tok_begin <= kFp8ResidualMaxUnitTokens;
-      if (is_short != (p.unit_filter == 2)) return;
-    }
   }
   const int n_vis = L - p.T + t_row + 1;  // dense: visible tokens of this row
 
@@ -779,6 +779,10 @@ mla_partial_kernel(const PartialParams p) {
   float m_seen = -INFINITY;        // running lane maximum, for the second pass
   float l_f = 0.f;                 // this half's sum of the unrounded weights (gives lse)
   float l_r = 0.f;                 // bf16: this half's sum of the rounded weights (normalizes O)
+  float l_q2 = 0.f;                // fp8 without residual: bound of this half's sum of squared weights
+  int top_sc = -1;                 // fp8 without residual: highest block exponent of a tile so far,
+  int top_tile = 0;                //   the first tile that reached it,
+  float top_q2 = 0.f;              //   and that tile's share of l_q2
   const float c_qk = p.qk_scale;   // softmax_scale * log2(e) [* q_scale * kv_scale]
   const int e8m0_one = 127;        // E8M0 scale 2^0 (a VGPR operand of the inline-asm products)
 
@@ -802,11 +806,12 @@ mla_partial_kernel(const PartialParams p) {
       else mfma_bf16_acc(sacc[0], a, __builtin_bit_cast(bf16x8_t, bq));
     }
   };
-  // PV product n of a tile with softmax output pt.
-  auto pv_mfma = [&](int n, const opnd_t& a, const PTile& pt) {
+  // PV product n of a tile with softmax output pt (resid_c: also the
+  // residual weights, fp8 only).
+  auto pv_mfma = [&](int n, const opnd_t& a, const PTile& pt, auto resid_c) {
     if constexpr (FP8) {
       oacc[n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pt.pb, oacc[n], 0, 0, 0, 127, 0, pt.sc);
-      if constexpr (RESID)
+      if constexpr (decltype(resid_c)::value)
         oacc[n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pt.pbl, oacc[n], 0, 0, 0, 127, 0, pt.scl);
     } else {
       const i32x4_t half = n & 1 ? i32x4_t{pt.pb[4], pt.pb[5], pt.pb[6], pt.pb[7]}
@@ -815,7 +820,7 @@ mla_partial_kernel(const PartialParams p) {
                                                              0, 0);
     }
   };
-  auto row_sum_mfma = [&](const PTile& pt) {
+  auto row_sum_mfma = [&](const PTile& pt, auto resid_c) {
     // The all-ones operand is rebuilt at each use rather than held live.
     const i32x8_t ones8 = {kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4,
                            kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4};
@@ -823,7 +828,7 @@ mla_partial_kernel(const PartialParams p) {
                              (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
     if constexpr (FP8) {
       mfma_f8_acc(lsum, ones8, pt.pb, e8m0_one, pt.sc);
-      if constexpr (RESID) mfma_f8_acc(lsum, ones8, pt.pbl, e8m0_one, pt.scl);
+      if constexpr (decltype(resid_c)::value) mfma_f8_acc(lsum, ones8, pt.pbl, e8m0_one, pt.scl);
     }
     (void)ones16;
   };
@@ -909,7 +914,7 @@ mla_partial_kernel(const PartialParams p) {
     st.prsum[tb] = 0.f;
   };
   // Stage "exponents of registers 4d .. 4d+3 of token block tb".
-  auto sm_exp = [&](f32x16_t (&sacc)[K::kTokBlocks], int tb, int d, SmState& st, PTile& pt) {
+  auto sm_exp = [&](f32x16_t (&sacc)[K::kTokBlocks], int tb, int d, SmState& st, PTile& pt, auto resid_c) {
     const int v = 4 * d;
     const float sh = st.shift[tb];
     const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[tb][v], c_qk, sh));
@@ -923,7 +928,7 @@ mla_partial_kernel(const PartialParams p) {
       w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
       pin(w);
       pt.pb[4 * tb + d] = w;
-      if constexpr (RESID) {
+      if constexpr (decltype(resid_c)::value) {
         // lo = e4m3(16 (P' - hi)): hi + lo/16 holds P' to about 2^-8.
         const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
         const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
@@ -955,12 +960,27 @@ mla_partial_kernel(const PartialParams p) {
   };
   // Stage "finish": the P operand's scales (lane half h carries token
   // block h's) and this half's unrounded weights join l_f.
-  auto sm_finish = [&](const SmState& st, PTile& pt) {
+  auto sm_finish = [&](const SmState& st, PTile& pt, int tile) {
     if constexpr (FP8) {
       pt.sc = h == 0 ? st.sc[0] : st.sc[1];
       pt.scl = pt.sc > 4 ? pt.sc - 4 : 0;
       l_f += st.psum[0] * __builtin_amdgcn_ldexpf(1.0f, st.sc[0] - 127) +
              st.psum[1] * __builtin_amdgcn_ldexpf(1.0f, st.sc[1] - 127);
+      if constexpr (!RESID) {
+        // A block's weights are psum * 2^e (e = sc - 127) in l_f's units and
+        // none exceeds 2^(8 + e), so their squares sum to at most
+        // psum * 2^(2e + 8); kept scaled by 2^-64 (e <= 64, so no overflow).
+        const float t2 = __builtin_amdgcn_ldexpf(st.psum[0], 2 * st.sc[0] - 310) +
+                         __builtin_amdgcn_ldexpf(st.psum[1], 2 * st.sc[1] - 310);
+        l_q2 += t2;
+        // The tile holding the row's heaviest block (by its exponent; the
+        // same in both halves of the row, so both pick the same tile).
+        const int tsc = max(st.sc[0], st.sc[1]);
+        const bool up = tsc > top_sc;
+        top_sc = up ? tsc : top_sc;
+        top_tile = up ? tile : top_tile;
+        top_q2 = up ? t2 : top_q2;
+      }
     } else {
       pt.sc = pt.scl = 0;
       l_f += st.psum[0];
@@ -971,22 +991,22 @@ mla_partial_kernel(const PartialParams p) {
   // unrolled): [mask], max, row, NEXP exponent stages; no-op past the end.
   constexpr int NSTAGE_BLOCK = 2 + NEXP;
   auto sm_block_stage = [&](int k, bool mask, f32x16_t (&sacc)[K::kTokBlocks], int i, int tb, bool& jumped,
-                            SmState& st, PTile& pt) {
+                            SmState& st, PTile& pt, auto resid_c) {
     if (mask) {
       if (k == 0) { sm_mask(sacc, i, tb); return; }
       k -= 1;
     }
     if (k == 0) sm_max(sacc, tb, st);
     else if (k == 1) sm_row(tb, jumped, st);
-    else if (k < 2 + NEXP) sm_exp(sacc, tb, k - 2, st, pt);
+    else if (k < 2 + NEXP) sm_exp(sacc, tb, k - 2, st, pt, resid_c);
   };
-  auto softmax_all = [&](f32x16_t (&sacc)[K::kTokBlocks], int i, bool& jumped, PTile& pt) {
+  auto softmax_all = [&](f32x16_t (&sacc)[K::kTokBlocks], int i, bool& jumped, PTile& pt, auto resid_c) {
     SmState st;
 #pragma unroll
     for (int tb = 0; tb < K::kTokBlocks; tb++)
 #pragma unroll
-      for (int k = 0; k < NSTAGE_BLOCK + 1; k++) sm_block_stage(k, true, sacc, i, tb, jumped, st, pt);
-    sm_finish(st, pt);
+      for (int k = 0; k < NSTAGE_BLOCK + 1; k++) sm_block_stage(k, true, sacc, i, tb, jumped, st, pt, resid_c);
+    sm_finish(st, pt, i);
   };
 
   // Finer stages for the feature-split step, whose schedule gives each one
@@ -1054,8 +1074,8 @@ mla_partial_kernel(const PartialParams p) {
   // (token block 0, then block 1) with the DMA of tile i+NS-1 spread between
   // its products and token block 0's softmax between block 1's products;
   // then the PV products of tile i with block 1's softmax between them.
-  auto pipe_step = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped,
-                       auto mask_c) __attribute__((always_inline)) {
+  auto pipe_step = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped, auto mask_c,
+                       auto resid_c) __attribute__((always_inline)) {
     constexpr bool mask = decltype(mask_c)::value;
     constexpr int KS = K::kQkSteps;
     // Tile i+1 resident (one tile may still be in flight behind it); every
@@ -1081,7 +1101,7 @@ mla_partial_kernel(const PartialParams p) {
       __builtin_amdgcn_sched_barrier(0);
       qk_mfma(sacc, n, qa[n % 3]);
       if (n == KS) mfma_drain(sacc[0]);          // block 0's chain ended one product ago
-      if (n > KS) sm_block_stage(n - KS - 1, mask, sacc, i + 1, 0, jumped, st, pn);
+      if (n > KS) sm_block_stage(n - KS - 1, mask, sacc, i + 1, 0, jumped, st, pn, resid_c);
       if (n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1090,14 +1110,14 @@ mla_partial_kernel(const PartialParams p) {
     for (int n = 0; n < NPV; n++) {
       if (n + 2 < NPV) va[(n + 2) % 3] = ld_pv(tv, n + 2);
       __builtin_amdgcn_sched_barrier(0);
-      pv_mfma(n, va[n % 3], pt);
+      pv_mfma(n, va[n % 3], pt, resid_c);
       if (n == 0) mfma_drain(sacc[1]);
-      if (n > 0) sm_block_stage(n - 1, mask, sacc, i + 1, 1, jumped, st, pn);
-      if (n == NSTAGE_BLOCK + 2) sm_finish(st, pn);
+      if (n > 0) sm_block_stage(n - 1, mask, sacc, i + 1, 1, jumped, st, pn, resid_c);
+      if (n == NSTAGE_BLOCK + 2) sm_finish(st, pn, i + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     static_assert(NSTAGE_BLOCK + 3 <= NPV, "block 1's stages fit between the PV products");
-    row_sum_mfma(pt);
+    row_sum_mfma(pt, resid_c);
     pt = pn;
   };
 
@@ -1186,7 +1206,7 @@ mla_partial_kernel(const PartialParams p) {
       __builtin_amdgcn_sched_barrier(0);
       qk_mfma(sacc, a, qa[a % 3]);
       if (a % 2 == 0 && a < 8) fs_exp(sacc, 1, 4 + a / 2, st, pt);
-      if (a == 7) sm_finish(st, pt);
+      if (a == 7) sm_finish(st, pt, i);
       if (a == 8) fs_write_p(pt);
       if (a % 2 == 1) dma_issue(src, nxt % NS, a / 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -1230,7 +1250,7 @@ mla_partial_kernel(const PartialParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     static_assert(FS_NSTAGE - 4 + 1 <= 8, "block 1's first stages fit phase C");
-    row_sum_mfma(pt);
+    row_sum_mfma(pt, std::false_type{});
     pt = pn;
     st = sn;
   };
@@ -1270,11 +1290,12 @@ mla_partial_kernel(const PartialParams p) {
     for (int n = 0; n < NPV; n++) {
       if (n + QD < NPV) va[(n + QD) % (QD + 1)] = ld_pv(tv, n + QD);
       __builtin_amdgcn_sched_barrier(0);
-      pv_mfma(n, va[n % (QD + 1)], pt);
+      pv_mfma(n, va[n % (QD + 1)], pt, std::false_type{});
       if (n == 0) mfma_drain(sacc[0]);           // the QK chain ended one product ago
       // stages at every third product from n = 1, then the finish
-      if (n >= 1 && (n - 1) % 3 == 0 && (n - 1) / 3 < NSB) sm_block_stage((n - 1) / 3, mask, sacc, i + 1, 0, jumped, st, pn);
-      if (n == 3 * NSB + 1) sm_finish(st, pn);
+      if (n >= 1 && (n - 1) % 3 == 0 && (n - 1) / 3 < NSB)
+        sm_block_stage((n - 1) / 3, mask, sacc, i + 1, 0, jumped, st, pn, std::false_type{});
+      if (n == 3 * NSB + 1) sm_finish(st, pn, i + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     static_assert(3 * (NSTAGE_BLOCK + 1) + 1 < NPV, "the bf16 softmax stages fit between the PV products");
@@ -1282,24 +1303,19 @@ mla_partial_kernel(const PartialParams p) {
   };
 
 
-  // ---- the tile loop, at most twice (second pass: exact reference)
-  for (int pass = 0; pass < 2; pass++) {
-#pragma unroll
-    for (int fb = 0; fb < 16; fb++) oacc[fb] = f32x16_t{};
-    lsum = f32x16_t{};
-    l_f = 0.f;
-    l_r = 0.f;
-    if (pass == 1) {
-      const float mrow = max_across_halves(m_seen);
-      m_ref = mrow == -INFINITY ? kNegBig : (FP8 ? ceilf(mrow) : mrow);
-    }
-    bool jumped = false;
-
+  // ---- the tile loop of one pass.  fs_c: the feature-split step (else
+  // every wave owns its rows' whole output); resid_c: fp8 weights also
+  // carry their e4m3 residual.
+  auto tile_loop = [&](bool& jumped, auto fs_c, auto resid_c) __attribute__((always_inline)) {
+    constexpr bool fs = decltype(fs_c)::value;
+    // Step-variant tags that depend on this lambda's arguments, so that only
+    // the steps a variant uses are instantiated.
+    using clean_t = std::integral_constant<bool, fs && !fs>;
+    using masked_t = std::integral_constant<bool, fs || !fs>;
     if constexpr (PIPE) {
       if (n_tiles > 0) {
         // Prologue: NS-1 tiles in flight (zero fills past the end keep the
         // count uniform), then QK and softmax of tile 0.
-        if (pass > 0) issue_first_tiles();
         wait_vmcnt<NI * (NS - 2)>();
         lds_barrier();
         f32x16_t sacc[K::kTokBlocks];
@@ -1318,7 +1334,7 @@ mla_partial_kernel(const PartialParams p) {
         }
         PTile pt;
         int i = 0;
-        if constexpr (FS) {
+        if constexpr (fs) {
           // Tile 0's softmax up to the hand-over point of the step (block 1's
           // last two exponent stages and the finish come in step 0).
           SmState st;
@@ -1327,26 +1343,26 @@ mla_partial_kernel(const PartialParams p) {
 #pragma unroll
             for (int k = 0; k < FS_NSTAGE + 1 - (tb == 1 ? 4 : 0); k++)
               fs_stage(k, true, sacc, 0, tb, jumped, st, pt);
-          for (; i + 1 < n_clean; i++) pipe_step_fs(i, sacc, pt, st, jumped, std::false_type{});
-          for (; i + 1 < n_tiles; i++) pipe_step_fs(i, sacc, pt, st, jumped, std::true_type{});
+          for (; i + 1 < n_clean; i++) pipe_step_fs(i, sacc, pt, st, jumped, clean_t{});
+          for (; i + 1 < n_tiles; i++) pipe_step_fs(i, sacc, pt, st, jumped, masked_t{});
           // Last tile: the rest of its softmax, publish, PV.
 #pragma unroll
           for (int d = 4; d < FS_NEXP; d++) fs_exp(sacc, 1, d, st, pt);
-          sm_finish(st, pt);
+          sm_finish(st, pt, n_tiles - 1);
           fs_write_p(pt);
         } else {
-          softmax_all(sacc, 0, jumped, pt);
+          softmax_all(sacc, 0, jumped, pt, resid_c);
           if constexpr (FP8) {
-            for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, std::false_type{});
-            for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, std::true_type{});
+            for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, clean_t{}, resid_c);
+            for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, masked_t{}, resid_c);
           } else {
-            for (; i + 1 < n_clean; i++) pipe_step_bf16(i, sacc, pt, jumped, std::false_type{});
-            for (; i + 1 < n_tiles; i++) pipe_step_bf16(i, sacc, pt, jumped, std::true_type{});
+            for (; i + 1 < n_clean; i++) pipe_step_bf16(i, sacc, pt, jumped, clean_t{});
+            for (; i + 1 < n_tiles; i++) pipe_step_bf16(i, sacc, pt, jumped, masked_t{});
           }
         }
 
         // Last tile: PV only.
-        if constexpr (FS) {
+        if constexpr (fs) {
           wait_lgkm0();
           lds_barrier();   // every P tile of the last tile published
           const LDS_AS uint8_t* tv = lds + ((n_tiles - 1) % NS) * kTileBytes;
@@ -1354,7 +1370,7 @@ mla_partial_kernel(const PartialParams p) {
 #pragma unroll
           for (int f = 0; f < 4; f++) vt[f] = fs_ld_v(tv, f);
           fs_pv_tile(vt, pt);
-          row_sum_mfma(pt);
+          row_sum_mfma(pt, clean_t{});
         } else {
           const LDS_AS uint8_t* tv = lds + ((n_tiles - 1) % NS) * kTileBytes;
           opnd_t va[3];
@@ -1364,10 +1380,10 @@ mla_partial_kernel(const PartialParams p) {
           for (int n = 0; n < NPV; n++) {
             if (n + 2 < NPV) va[(n + 2) % 3] = ld_pv(tv, n + 2);
             __builtin_amdgcn_sched_barrier(0);
-            pv_mfma(n, va[n % 3], pt);
+            pv_mfma(n, va[n % 3], pt, resid_c);
             __builtin_amdgcn_sched_barrier(0);
           }
-          row_sum_mfma(pt);
+          row_sum_mfma(pt, resid_c);
         }
         wait_vmcnt<0>();   // the zero fills past the end must land before the LDS is reused
       }
@@ -1379,7 +1395,6 @@ mla_partial_kernel(const PartialParams p) {
       // one tile in flight at a time).  Past the end the slot gets a zero
       // fill, which keeps the wait a constant.
       static_assert(NS == 2, "two-slot loop");
-      if (pass > 0) issue_first_tiles();
       for (int i = 0; i < n_tiles; i++) {
         wait_vmcnt<0>();
         if (RG > 1) lds_barrier();   // tile i complete; every wave is done with tile i-1's slot
@@ -1408,7 +1423,7 @@ mla_partial_kernel(const PartialParams p) {
           drain_scores(sacc);
         }
         PTile pt;
-        softmax_all(sacc, i, jumped, pt);
+        softmax_all(sacc, i, jumped, pt, resid_c);
         opnd_t va[3];
         va[0] = ld_pv(tile, 0);
         va[1] = ld_pv(tile, 1);
@@ -1416,25 +1431,172 @@ mla_partial_kernel(const PartialParams p) {
         for (int n = 0; n < NPV; n++) {
           if (n + 2 < NPV) va[(n + 2) % 3] = ld_pv(tile, n + 2);
           __builtin_amdgcn_sched_barrier(0);
-          pv_mfma(n, va[n % 3], pt);
+          pv_mfma(n, va[n % 3], pt, resid_c);
           __builtin_amdgcn_sched_barrier(0);
         }
-        row_sum_mfma(pt);
+        row_sum_mfma(pt, resid_c);
       }
       wait_vmcnt<0>();   // the zero fill past the end must land before the LDS is reused
+    }
+  };
+
+  // ---- one tile of the fix pass: its DMA into ring slot 0, QK, the
+  // softmax weights against the unchanged m_ref, then only the products of
+  // the residual weights (PV and the row sum).
+  auto fix_tile = [&](int t) __attribute__((always_inline)) {
+    if constexpr (kFixTiles) {
+      issue_tile(t, 0);
+      wait_vmcnt<0>();
+      lds_barrier();
+      f32x16_t sacc[K::kTokBlocks];
+      {
+        opnd_t qa[3];
+        qa[0] = ld_qk(lds, 0);
+        qa[1] = ld_qk(lds, 1);
+#pragma unroll
+        for (int n = 0; n < NQK; n++) {
+          if (n + 2 < NQK) qa[(n + 2) % 3] = ld_qk(lds, n + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          qk_mfma(sacc, n, qa[n % 3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        drain_scores(sacc);
+      }
+      PTile pt;
+      SmState st;
+      bool no_jump = false;   // pass 0 already judged these scores
+#pragma unroll
+      for (int tb = 0; tb < K::kTokBlocks; tb++)
+#pragma unroll
+        for (int k = 0; k < NSTAGE_BLOCK + 1; k++)
+          sm_block_stage(k, true, sacc, t, tb, no_jump, st, pt, std::true_type{});
+      const int sc = h == 0 ? st.sc[0] : st.sc[1];
+      pt.scl = sc > 4 ? sc - 4 : 0;
+      const i32x8_t ones8 = {kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4,
+                             kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4, kE4m3OnesX4};
+      mfma_f8_acc(lsum, ones8, pt.pbl, e8m0_one, pt.scl);
+      if constexpr (FS) {
+        // Publish this row block's residual tile; every wave then applies
+        // all four to its feature quarter.
+        LDS_AS i32x4_t* dst = (LDS_AS i32x4_t*)(pbuf + wave * 2048 + lane * 32);
+        dst[0] = i32x4_t{pt.pbl[0], pt.pbl[1], pt.pbl[2], pt.pbl[3]};
+        dst[1] = i32x4_t{pt.pbl[4], pt.pbl[5], pt.pbl[6], pt.pbl[7]};
+        scbuf[wave * 64 + lane] = pt.scl;
+        wait_lgkm0();
+        lds_barrier();
+        i32x8_t vt[4];
+#pragma unroll
+        for (int f = 0; f < 4; f++) vt[f] = fs_ld_v(lds, f);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          i32x8_t pb = pt.pbl;
+          int scq = pt.scl;
+          if (r > 0) fs_read_p((wave + r) & 3, pb, scq);
+#pragma unroll
+          for (int f = 0; f < 4; f++) fs_pv_mfma(r, f, vt[f], pb, scq);
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NPV; n++)
+          oacc[n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ld_pv(lds, n), pt.pbl, oacc[n], 0, 0, 0, 127,
+                                                                    0, pt.scl);
+      }
+      mfma_drain(lsum);
+      lds_barrier();   // every wave is done with slot 0 and the P buffer
+    }
+  };
+
+  // ---- the passes.  Pass 0 uses the kernel's own step.  A second pass
+  // reruns the unit when a row's weights need more than pass 0 gave them:
+  //  * a row's block maximum rose more than 2^64 above its reference (the
+  //    O accumulator's headroom): the rerun takes the exact row maximum;
+  //  * fp8 without the residual product: the rounding of each weight to
+  //    e4m3 (up to 2^-4 relative) stays far below the output tolerance
+  //    while the weight is spread over many tokens, but not when a few
+  //    tokens carry most of it.  Pass 0 bounds sum_j w_j^2 (w the
+  //    normalized weights) from each block's sums; above 2^-7 the unit is
+  //    rerun with the residual product (each weight to about 2^-8), in the
+  //    plain four-wave step when pass 0 was the feature split.
+  // Rows of N(0,1) data in units of more than 16384 tokens stay near 2^-9.
+  constexpr bool kRedoResid = FP8 && !RESID;
+  bool fs_layout = FS;             // O is held in the feature-split layout
+  bool redone = false;             // pass 1 ran
+  for (int pass = 0; pass < 2; pass++) {
+#pragma unroll
+    for (int fb = 0; fb < 16; fb++) oacc[fb] = f32x16_t{};
+    lsum = f32x16_t{};
+    l_f = 0.f;
+    l_r = 0.f;
+    l_q2 = 0.f;
+    if (pass == 1) {
+      const float mrow = max_across_halves(m_seen);
+      m_ref = mrow == -INFINITY ? kNegBig : (FP8 ? ceilf(mrow) : mrow);
+    }
+    bool jumped = false;
+    if (pass > 0) issue_first_tiles();
+    if constexpr (kRedoResid) {
+      if (pass == 0) {
+        tile_loop(jumped, std::integral_constant<bool, FS>{}, std::false_type{});
+      } else {
+        fs_layout = false;
+        redone = true;
+        tile_loop(jumped, std::false_type{}, std::true_type{});
+      }
+    } else {
+      tile_loop(jumped, std::integral_constant<bool, FS>{}, std::integral_constant<bool, RESID>{});
     }
     if constexpr (FP8) mfma_drain(lsum);
 
     // ---- second pass needed?  (workgroup-uniform: all waves share the DMA)
     if (pass == 1) break;
-    const bool wave_jump = __builtin_amdgcn_ballot_w64(jumped && row_ok) != 0;
+    bool need = jumped;
+    bool fix = false;
+    if constexpr (kRedoResid) {
+      // sum_j w_j^2 <= q2 / l^2 with both in the units of sm_finish.  Most
+      // rows above the bound owe it to one heavy tile: adding the residual
+      // product of that tile alone (the fix pass below) is enough when the
+      // rest of the row stays under the bound; otherwise the unit reruns.
+      const float lt = sum_across_halves(l_f) * 0x1p-32f;
+      const float q2 = sum_across_halves(l_q2);
+      const float q2_top = sum_across_halves(top_q2);
+      const float lim = kFp8RedoSumSq * lt * lt;
+      need |= q2 - q2_top > lim;
+      fix = q2 > lim;
+    }
+    const bool wave_jump = __builtin_amdgcn_ballot_w64(need && row_ok) != 0;
     if (threadIdx.x == 0) *redo_flag = 0;
+    if constexpr (kFixTiles) {
+      if (threadIdx.x < kFixWords) fix_map[threadIdx.x] = 0u;
+    }
     __syncthreads();
     if (wave_jump && lane == 0) *redo_flag = 1;
+    if constexpr (kFixTiles) {
+      if (fix && row_ok && h == 0) __hip_atomic_fetch_or(&fix_map[top_tile >> 5], 1u << (top_tile & 31),
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     __syncthreads();
     const int redo = *redo_flag;
     __syncthreads();
     if (!redo) break;
+  }
+
+  // ---- fix pass (fp8 without the residual product): the residual product
+  // of each marked tile, added to what pass 0 accumulated.  Pass 0 reached
+  // every mark with the same reference m_ref, so recomputing the tile gives
+  // the same scores and the same e4m3 weights, and the residual completes
+  // them to about 2^-8 exactly as a residual-product pass would.  Rare:
+  // N(0,1) data marks about one row in 400, one tile each.
+  if constexpr (kFixTiles) {
+    if (!redone && n_tiles > 0) {
+      for (int wd = 0; wd < (n_tiles + 31) / 32; wd++) {
+        uint32_t bits = __builtin_amdgcn_readfirstlane(fix_map[wd]);
+        while (bits != 0u) {
+          const int t = wd * 32 + __builtin_ctz(bits);
+          bits &= bits - 1u;
+          fix_tile(t);
+        }
+      }
+    }
   }
 
   // ---- epilogue: normalize, write final output or the split partial
@@ -1530,7 +1692,7 @@ mla_partial_kernel(const PartialParams p) {
     }
   };
 
-  if constexpr (FS) {
+  if (FS && fs_layout) {
     // Row block rq's normalizer lives in wave rq; pass them through LDS
     // (the P tiles are dead by now).
     LDS_AS float* invbuf = (LDS_AS float*)pbuf;

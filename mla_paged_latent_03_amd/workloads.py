@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field
-from typing import List, Optional, Sequence, Tuple, Union
+from typing import Callable, List, Optional, Sequence, Tuple, Union
 
 import torch
 
@@ -133,8 +133,14 @@ def make_inputs(B: int, H: int, T: int, seq_lens: Union[Sequence[int], Tuple[int
                 kv_dtype: str = "bf16", out_dtype: str = "bf16", topk: Optional[int] = None,
                 seed: int = 0, device: Union[str, torch.device] = "cpu", block_size: int = PAGE,
                 softmax_scale: float = DEFAULT_SOFTMAX_SCALE, extra_pages: int = 0,
-                extra_table_cols: int = 0, poison: bool = False, name: str = "custom") -> DecodeInputs:
+                extra_table_cols: int = 0, poison: bool = False, name: str = "custom",
+                edit_values: Optional[Callable] = None) -> DecodeInputs:
     """Draw one decode batch.
+
+    ``edit_values(kv, q, block_table, lens)``, if given, may change the fp32
+    values in place after they are drawn and before they are rounded (kv
+    [pool, 64, 576], q [B, T, H, 576] on ``device``; block_table and lens on
+    the CPU); tests use it to shape particular rows.
 
     ``poison`` fills every page slot no sequence owns (the pages beyond the
     pool, and the slots past L_b in each sequence's last page) with NaN, so a
@@ -176,6 +182,8 @@ def make_inputs(B: int, H: int, T: int, seq_lens: Union[Sequence[int], Tuple[int
     # Values.
     kv32 = torch.randn((pool, block_size, D_TOKEN), generator=g_val, device=device, dtype=torch.float32)
     q32 = torch.randn((B, T, H, D_TOKEN), generator=g_val, device=device, dtype=torch.float32)
+    if edit_values is not None:
+        edit_values(kv32, q32, block_table, lens)
     q_scale = kv_scale = 1.0
     if kv_dtype == "bf16":
         kv = kv32.to(torch.bfloat16)

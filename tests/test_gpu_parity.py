@@ -41,6 +41,13 @@ def check_full(inp, num_kv_splits=0, what=""):
     return compare(out, lse, ref_o, ref_l, inp.kv_dtype, what=what)
 
 
+def fixed_unit_tokens(max_seq_len, splits):
+    """Tokens of a work unit when a call cuts fixed chunks (the rule of the
+    C header for calls that are not cut by the actual lengths)."""
+    pages = -(-max_seq_len // 64)
+    return -(-pages // splits) * 64
+
+
 # ------------------------------------------------------------------ tiny workload, every split count
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 7, 0])
@@ -186,6 +193,103 @@ def test_fp8_long_units_without_residual_product():
     compare(out, lse, ref_o, ref_l, "fp8", rows=rows, what="fp8 long units")
 
 
+def _plant_dominant_tokens(T, n_dominant, seed, rows=((0, 0),), offset_nats=6.0):
+    """edit_values hook: in every sequence b, n_dominant(b) cache positions
+    (after the first 64, visible to every draft token) get logits about
+    `offset_nats` above the largest other logit of each listed row (t, h),
+    within +-0.3 nats of each other, so those rows are dominated by a few
+    comparable tokens.  The tokens keep their random latents; only their
+    rope part is set (along the row's rope query), in fp32 before rounding."""
+    sigma = wl.DEFAULT_SOFTMAX_SCALE
+
+    def edit(kv, q, block_table, lens):
+        g = torch.Generator().manual_seed(seed)
+        for b in range(q.shape[0]):
+            L = int(lens[b])
+            n_vis = L - T + 1
+            if n_vis <= 64 + 8:
+                continue
+            pages = block_table[b, :(L + 63) // 64].long().to(kv.device)
+            toks = kv[pages].reshape(-1, wl.D_TOKEN)[:n_vis]
+            for (t, h) in rows:
+                qr = q[b, t, h]
+                top = float((toks @ qr).max()) * sigma
+                pos = (torch.randperm(n_vis - 64, generator=g)[:n_dominant(b)] + 64).tolist()
+                for j in pos:
+                    target = top + offset_nats + (float(torch.rand(1, generator=g)) - 0.5) * 0.6
+                    pg, sl = int(block_table[b, j // 64]), j % 64
+                    c = kv[pg, sl, :wl.D_LATENT]
+                    qn, qp = qr[:wl.D_LATENT], qr[wl.D_LATENT:]
+                    lam = (target / sigma - float(qn @ c)) / float(qp @ qp)
+                    kv[pg, sl, wl.D_LATENT:] = lam * qp
+                toks = kv[pages].reshape(-1, wl.D_TOKEN)[:n_vis]
+    return edit
+
+
+@pytest.mark.parametrize("lens,kind", [((20000, 40000), "dominant"), ((20000, 30000), "sink"),
+                                       ((20000, 24000), "jump")])
+def test_feature_split_long_units_dominant_tokens_and_jump(lens, kind):
+    """The headline kernel (four-wave feature-split fp8 step, no residual
+    product: units over 16384 tokens) on rows whose weight sits on 2-4
+    comparable tokens (the unit reruns with the residual product), on rows
+    with one heavy token (the residual product of its tile is added), and on
+    a logit more than 2^64 (log2 domain) above the first tile's (the unit
+    reruns against the exact maximum); every element of the shaped rows is
+    compared."""
+    B, T, H = 16, 4, 32
+    edit = None
+    if kind == "dominant":
+        edit = _plant_dominant_tokens(T, lambda b: 2 + b % 3, seed=71, rows=((0, 0), (T - 1, H - 1)))
+    elif kind == "sink":
+        edit = _plant_dominant_tokens(T, lambda b: 1, seed=73, rows=((0, 0), (T - 1, H - 1)), offset_nats=3.0)
+    inp = wl.make_inputs(B, H, T, lens, kv_dtype="fp8", out_dtype="f32", seed=71 + len(kind), device=DEV,
+                         edit_values=edit)
+    assert binding.launch_waves(B, T, H, inp.max_len, 0, True) == 4
+    assert fixed_unit_tokens(int(inp.seq_lens.min()), 1) > 16384
+    cpu = inp.to("cpu")
+    if kind == "jump":
+        _plant_large_logit(cpu, 12345)
+        inp = cpu.to(DEV)
+    out, lse = run_case(inp, 1, "feature split, %s, units %s" % (kind, lens))
+    R = T * H
+    shaped = np.array([b * R + r for b in range(B) for r in (0, R - 1)], dtype=np.int64)
+    rows = np.unique(np.concatenate([shaped, np.arange(R, 2 * R), sample_rows(B * R, 64, seed=72)]))
+    _say("[gpu] oracle on %d rows" % rows.size)
+    ref_o, ref_l = oracle_rows(cpu, rows=rows)
+    if kind == "jump":
+        assert np.max(ref_l) > 80.0
+    else:
+        # the planted tokens carry much of each shaped row's weight
+        assert np.all(ref_l[np.searchsorted(rows, shaped)] > 9.0)
+    e = compare(out, lse, ref_o, ref_l, "fp8", rows=rows, what="feature split %s" % kind)
+    _say("[gpu] feature split %s: max |out - oracle| %.4g, lse rel %.3g" % ((kind,) + e))
+
+
+@pytest.mark.parametrize("H,waves", [(16, 2), (64, 1)])
+@pytest.mark.parametrize("kind", ["dominant", "sink", "jump", "short"])
+def test_narrow_blocks_long_fp8_units(H, waves, kind):
+    """One- and two-wave fp8 kernels without the residual product (units
+    over 16384 tokens): rows dominated by a few tokens, a large logit jump,
+    and short sequences in the same call (their units rerun with the
+    residual product)."""
+    T = 1
+    lens = [20000, 300, 18000, 1] if kind == "short" else [20000, 17500, 19000, 22000]
+    B = len(lens)
+    edit = None
+    if kind == "dominant":
+        edit = _plant_dominant_tokens(T, lambda b: 2 + b % 3, seed=81 + H)
+    elif kind == "sink":
+        edit = _plant_dominant_tokens(T, lambda b: 1, seed=83 + H, offset_nats=3.0)
+    inp = wl.make_inputs(B, H, T, lens, kv_dtype="fp8", out_dtype="f32", seed=81 + H + len(kind),
+                         poison=True, edit_values=edit)
+    if kind == "jump":
+        _plant_large_logit(inp, 9999)
+    assert binding.launch_waves(B, T, H, inp.max_len, 0, True) == waves
+    assert fixed_unit_tokens(inp.max_len, 1) > 16384
+    e = check_full(inp, 1, "%d-wave long fp8 units, %s" % (waves, kind))
+    _say("[gpu] %d-wave %s: max |out - oracle| %.4g, lse rel %.3g" % ((waves, kind) + e))
+
+
 @pytest.mark.parametrize("lens,splits", [([300, 9000, 20000, 1], 1), ([40000] * 3 + [300], 2)])
 def test_fp8_short_sequence_among_long_units(lens, splits):
     """A call planned for long fp8 units (no residual product) with a short
@@ -320,6 +424,8 @@ def test_degenerate_head_counts_and_longest_draft(H, T, kv_dtype):
     (16, 1, [100, 3000], 256, 2),
     (128, 1, [5000, 70], 512, 0),
     (64, 2, [900, 2500], 192, 0),      # MTP with per-token index lists
+    (32, 4, [700, 3000], 256, 0),
+    (16, 8, [300, 5000, 90], 512, 0),
     (32, 1, [4100], 4096, 0),          # K above one workgroup's index table: forced splits
 ])
 def test_sparse_shapes(H, T, lens, K, splits):
@@ -332,6 +438,8 @@ def test_sparse_shapes(H, T, lens, K, splits):
     (16, 1, [100, 3000], 256, 2),
     (128, 1, [5000, 70], 512, 0),
     (64, 2, [900, 2500], 192, 0),      # MTP with per-token index lists
+    (32, 4, [700, 3000], 256, 0),
+    (16, 8, [300, 5000, 90], 512, 0),
     (32, 1, [4100], 4096, 0),          # K above one workgroup's index table: forced splits
 ])
 def test_sparse_fp8_shapes(H, T, lens, K, splits):
@@ -398,8 +506,12 @@ FOUR_WAVE = [
     ("bf16", 32, 128, 8, (60, 900), 0),
     ("fp8", 256, 32, 4, (3, 700), 0),
     ("fp8", 256, 128, 1, (32, 330), 0),
+    ("fp8", 32, 32, 4, (3, 700), 0),
     ("sparse", 256, 128, 1, (100, 900), 96),
+    ("sparse", 16, 128, 1, (100, 900), 96),
     ("sparse_fp8", 256, 128, 1, (100, 900), 96),
+    ("sparse_fp8", 16, 128, 1, (100, 900), 96),
+    ("sparse_fp8", 16, 128, 2, (100, 900), 160),
 ]
 
 
@@ -410,7 +522,8 @@ def test_four_wave_variants(kind, B, H, T, lens, K):
                          poison=True)
     assert binding.launch_waves(B, T, H, inp.max_len, K, kv_dtype == "fp8") == 4
     out, lse = run_case(inp, 0, "four-wave %s" % kind)
-    rows = sample_rows(B * T * H, 160, seed=B + H)
+    # every row of the smaller batches, a sample of the larger ones
+    rows = None if B * T * H <= 4096 else sample_rows(B * T * H, 1024, seed=B + H)
     ref_o, ref_l = oracle_rows(inp, rows=rows)
     compare(out, lse, ref_o, ref_l, kv_dtype, rows=rows, what="four-wave %s" % kind)
 
@@ -457,24 +570,30 @@ def test_large_logit_jump_reruns_against_exact_maximum(kind, B, H, T, waves):
 
 # ------------------------------------------------------------------ graph capture
 
-@pytest.mark.parametrize("lens", [[100, 800, 2000, 64], [40000, 300, 20000, 1]])
-def test_hip_graph_replay_matches_eager(lens):
-    """Short units (one launch with the residual product), and long units
-    next to short ones (the long-unit and residual launches), then the merge,
-    all captured in one graph."""
-    inp = wl.make_inputs(4, 32, 4, lens, kv_dtype="fp8", out_dtype="bf16", seed=17).to(DEV)
-    _say("[gpu] graph capture, lengths %s" % lens)
-    eager_o, eager_l, ws = binding.decode(inp, num_kv_splits=3)
+@pytest.mark.parametrize("lens,splits", [([100, 800, 2000, 64], 3), ([40000, 300, 20000, 1], 2)])
+def test_hip_graph_replay_matches_eager(lens, splits):
+    """fp8 calls captured in one graph with their merge: short units (the
+    residual-product kernel), and units over 16384 tokens next to short ones
+    (the feature-split kernel, whose short units rerun with the residual
+    product)."""
+    B, T, H = 4, 4, 32
+    long_units = fixed_unit_tokens(max(lens), splits) > 16384
+    if long_units:
+        assert binding.launch_waves(B, T, H, max(lens), 0, True) == 4
+    inp = wl.make_inputs(B, H, T, lens, kv_dtype="fp8", out_dtype="bf16", seed=17).to(DEV)
+    _say("[gpu] graph capture, lengths %s, %d splits, long units %s" % (lens, splits, long_units))
+    assert long_units == (max(lens) > 20000)
+    eager_o, eager_l, ws = binding.decode(inp, num_kv_splits=splits)
     torch.cuda.synchronize()
     out = torch.empty_like(eager_o)
     lse = torch.empty_like(eager_l)
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
-        binding.decode(inp, num_kv_splits=3, out=out, lse=lse, workspace=ws)   # warm the stream
+        binding.decode(inp, num_kv_splits=splits, out=out, lse=lse, workspace=ws)   # warm the stream
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
-            binding.decode(inp, num_kv_splits=3, out=out, lse=lse, workspace=ws, stream=s)
+            binding.decode(inp, num_kv_splits=splits, out=out, lse=lse, workspace=ws, stream=s)
     for rep in range(4):
         out.fill_(float("nan"))
         torch.cuda.synchronize()
@@ -483,6 +602,8 @@ def test_hip_graph_replay_matches_eager(lens):
         assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), "replay %d differs" % rep
         binding.decode(inp, num_kv_splits=1)   # unrelated eager work between replays
         torch.cuda.synchronize()
+    ref_o, ref_l = oracle_rows(inp.to("cpu"))
+    compare(eager_o, eager_l, ref_o, ref_l, "fp8", what="graph replay %s" % lens)
 
 
 # ------------------------------------------------------------------ full-size workloads (sampled rows)
@@ -500,11 +621,15 @@ def test_full_size_workload_sampled_rows(name):
     assert torch.isfinite(out.float()).all().item()
     assert torch.isfinite(lse).all().item()
     n_total = inp.B * inp.T * inp.H
-    rows = sample_rows(n_total, 48, seed=sum(name.encode()))
+    R = inp.T * inp.H
+    # all rows of the first and last sequences, and 512 random others
+    rows = np.unique(np.concatenate([np.arange(0, R), np.arange(n_total - R, n_total),
+                                     sample_rows(n_total, 512, seed=sum(name.encode()))]))
     cpu = inp.to("cpu")
     _say("[gpu] full-size %s: oracle on %d rows" % (name, rows.size))
     ref_o, ref_l = oracle_rows(cpu, rows=rows)
-    compare(out, lse, ref_o, ref_l, inp.kv_dtype, rows=rows, what=name)
+    e = compare(out, lse, ref_o, ref_l, inp.kv_dtype, rows=rows, what=name)
+    _say("[gpu] full-size %s: max |out - oracle| %.4g, lse rel %.3g over %d rows" % ((name,) + e + (rows.size,)))
 
 
 # ------------------------------------------------------------------ two-stage form
