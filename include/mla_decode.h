@@ -103,7 +103,8 @@ typedef enum {
   MLA_ERR_INVALID_ARGUMENT = 1,
   MLA_ERR_UNSUPPORTED = 2,
   MLA_ERR_WORKSPACE_TOO_SMALL = 3,
-  MLA_ERR_HIP = 4
+  MLA_ERR_HIP = 4,
+  MLA_ERR_SCRATCH_LIMIT = 5   /* mla_decode_fp8_noalloc: partials exceed its static buffer */
 } mla_status_t;
 
 /* Output element type of `out`. */
@@ -213,6 +214,29 @@ mla_status_t mla_decode_fp8(const void* q_nope, const void* q_pe, const void* kv
                             float q_scale, float kv_scale, void* out, int out_dtype, float* lse,
                             void* workspace, size_t workspace_bytes, int num_kv_splits,
                             void* stream);
+
+/*
+ * mla_decode_fp8 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same arguments without workspace / workspace_bytes, the same plan,
+ * kernels and results.  The split partials go to a static device buffer of
+ * 64 MiB that the library holds on each GPU it runs on until the process
+ * ends; its address is looked up once per device, on the first call made
+ * with that device current.  The call allocates nothing.
+ *   A call whose partials (mla_workspace_size(B, T, H, max_seq_len, 0, 1,
+ * num_kv_splits) bytes) exceed 64 MiB returns MLA_ERR_SCRATCH_LIMIT before
+ * anything is enqueued; pass a smaller num_kv_splits to fit.  Every call on
+ * one GPU shares that GPU's buffer, so calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * give undefined results.  Nothing in the buffer has to start at a given
+ * value: each call writes every partial it later reads.
+ */
+mla_status_t mla_decode_fp8_noalloc(const void* q_nope, const void* q_pe, const void* kv_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens, int batch,
+                                    int q_len, int num_heads, int num_blocks, int block_size,
+                                    int max_blocks_per_seq, int max_seq_len, float softmax_scale,
+                                    float q_scale, float kv_scale, void* out, int out_dtype, float* lse,
+                                    int num_kv_splits, void* stream);
 
 /*
  * Top-k sparse bf16 decode.  topk_indices [B, T, K] int32 lists, per query

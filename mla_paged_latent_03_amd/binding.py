@@ -16,11 +16,14 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
 
-MLA_OK, MLA_ERR_INVALID_ARGUMENT, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP = range(5)
+(MLA_OK, MLA_ERR_INVALID_ARGUMENT, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP,
+ MLA_ERR_SCRATCH_LIMIT) = range(6)
+STATIC_SCRATCH_BYTES = 64 << 20
 MLA_OUT_BF16, MLA_OUT_F32 = 0, 1
 MAX_KV_SPLITS = 256
 EXPORTS = ("mla_status_string", "mla_num_kv_splits", "mla_launch_waves", "mla_workspace_size",
-           "mla_num_kv_splits_baseline", "mla_decode", "mla_decode_fp8", "mla_sparse_decode", "mla_merge_partials")
+           "mla_num_kv_splits_baseline", "mla_decode", "mla_decode_fp8", "mla_decode_fp8_noalloc",
+           "mla_sparse_decode", "mla_sparse_decode_fp8", "mla_merge_partials")
 
 _lib = None
 
@@ -55,6 +58,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 7 + common_tail
     lib.mla_decode_fp8.restype = c_int
     lib.mla_decode_fp8.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_float, c_float] + common_tail[1:]
+    lib.mla_decode_fp8_noalloc.restype = c_int
+    lib.mla_decode_fp8_noalloc.argtypes = ([vp, vp, vp, vp, vp] + [c_int] * 7 + [c_float, c_float, c_float, vp, c_int, vp,
+                                           c_int, vp])
     lib.mla_sparse_decode.restype = c_int
     lib.mla_sparse_decode.argtypes = [vp, vp, vp, vp, vp, vp, c_int] + [c_int] * 7 + common_tail
     lib.mla_sparse_decode_fp8.restype = c_int
@@ -143,6 +149,19 @@ def mla_decode_fp8(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len, s
                                float(q_scale), float(kv_scale), _ptr(out), _out_code(out), _ptr(lse),
                                _ptr(workspace), ws_bytes, int(num_kv_splits), _stream(stream))
     _check(st, "mla_decode_fp8")
+
+
+def mla_decode_fp8_noalloc(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len, softmax_scale, q_scale,
+                           kv_scale, out, lse=None, num_kv_splits=0, stream=None):
+    """mla_decode_fp8 with the split partials in the library's static buffer
+    (mla_decode_fp8_noalloc): no workspace argument, nothing allocated."""
+    B, T, H, _ = q_nope.shape
+    NB, P, _ = kv_cache.shape
+    st = load().mla_decode_fp8_noalloc(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+                                       B, T, H, NB, P, block_table.shape[1], int(max_seq_len), float(softmax_scale),
+                                       float(q_scale), float(kv_scale), _ptr(out), _out_code(out), _ptr(lse),
+                                       int(num_kv_splits), _stream(stream))
+    _check(st, "mla_decode_fp8_noalloc")
 
 
 def mla_sparse_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, topk_indices, max_seq_len, softmax_scale,

@@ -275,6 +275,7 @@ const char* mla_status_string(mla_status_t status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MLA_ERR_HIP: return "HIP launch failure";
+    case MLA_ERR_SCRATCH_LIMIT: return "call needs more split workspace than the static 64 MiB buffer";
   }
   return "unknown status";
 }
@@ -327,6 +328,25 @@ mla_status_t mla_decode_fp8(const void* q_nope, const void* q_pe, const void* kv
   return run(Kind::kFp8, q_nope, q_pe, kv_cache, block_table, seq_lens, nullptr, 0, batch, q_len, num_heads,
              num_blocks, block_size, max_blocks_per_seq, max_seq_len, softmax_scale, q_scale, kv_scale, out,
              out_dtype, lse, workspace, workspace_bytes, num_kv_splits, stream);
+}
+
+mla_status_t mla_decode_fp8_noalloc(const void* q_nope, const void* q_pe, const void* kv_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens, int batch, int q_len,
+                                    int num_heads, int num_blocks, int block_size, int max_blocks_per_seq,
+                                    int max_seq_len, float softmax_scale, float q_scale, float kv_scale, void* out,
+                                    int out_dtype, float* lse, int num_kv_splits, void* stream) {
+  // Sizes the plan first: a call whose partials do not fit the static buffer
+  // is refused before anything is looked up or enqueued.  Invalid arguments
+  // fall through to run(), which reports them.
+  Plan pl;
+  void* ws = nullptr;
+  if (batch > 0 && make_plan(batch, q_len, num_heads, max_seq_len, 0, true, num_kv_splits, &pl)) {
+    if (pl.ws_bytes > mla::kStaticScratchBytes) return MLA_ERR_SCRATCH_LIMIT;
+    if (pl.ws_bytes > 0 && mla::static_scratch(&ws) != hipSuccess) return MLA_ERR_HIP;
+  }
+  return run(Kind::kFp8, q_nope, q_pe, kv_cache, block_table, seq_lens, nullptr, 0, batch, q_len, num_heads,
+             num_blocks, block_size, max_blocks_per_seq, max_seq_len, softmax_scale, q_scale, kv_scale, out,
+             out_dtype, lse, ws, ws ? mla::kStaticScratchBytes : 0, num_kv_splits, stream);
 }
 
 mla_status_t mla_sparse_decode(const void* q_nope, const void* q_pe, const void* kv_cache,

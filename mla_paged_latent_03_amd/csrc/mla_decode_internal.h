@@ -56,6 +56,12 @@ struct MergeParams {
 // without it and rerun a unit with it when its weights need it.
 constexpr int kFp8ResidualMaxUnitTokens = 16384;
 
+// Size of the static split workspace behind mla_decode_fp8_noalloc.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+
+// Device address of this GPU's static workspace (looked up once per device).
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_partial_kernel(const PartialParams& p, bool fp8, bool sparse, int rg, bool resid, int grid,
                                  hipStream_t stream);
 hipError_t launch_merge_kernel(const MergeParams& p, hipStream_t stream);

@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "mla_decode_internal.h"
@@ -1862,6 +1863,37 @@ hipError_t launch_merge_kernel(const MergeParams& p, hipStream_t stream) {
   const int64_t blocks = (p.n_rows + 3) / 4;
   void* args[] = {(void*)&p};
   return hipLaunchKernel((const void*)&mla_merge_kernel, dim3((unsigned)blocks), dim3(256), args, 0, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Static split workspace of the allocation-free entry point.  One copy per
+// GPU, at that GPU's own address, held until the process ends.  Host code
+// must not use the array's name as a device address: it is a host-side
+// stand-in.  The device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is kept per device.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace mla

@@ -227,3 +227,20 @@ def test_asm_hazard_scan_flags_m0_and_sgpr_hazards():
     nt_sparse = _asm("s_add_i32 m0, s37, 0x400", ";;#ASMSTART", "global_load_lds_dwordx4 v[2:3], off nt",
                      ";;#ASMEND")
     assert len(hz.scan(nt_sparse)) == 1
+
+
+def test_noalloc_refuses_partials_beyond_its_static_buffer(lib):
+    """mla_decode_fp8_noalloc sizes the plan before anything else: partials
+    over 64 MiB are refused with their own status, before any HIP call (the
+    pointers here are never dereferenced)."""
+    fake = ctypes.c_void_p(0x1000)
+    B, T, H, L = 64, 4, 32, 80000
+    assert binding.workspace_size(B, T, H, L, 0, True, 8) > binding.STATIC_SCRATCH_BYTES
+    st = lib.mla_decode_fp8_noalloc(fake, fake, fake, fake, fake, B, T, H, 100, 64, 1250, L, 0.07, 1.0, 1.0, fake,
+                                    0, fake, 8, None)
+    assert st == binding.MLA_ERR_SCRATCH_LIMIT
+    assert "static" in binding.status_string(st)
+    # invalid arguments keep their usual status
+    st = lib.mla_decode_fp8_noalloc(fake, fake, fake, fake, fake, B, 9, H, 100, 64, 1250, L, 0.07, 1.0, 1.0, fake,
+                                    0, fake, 2, None)
+    assert st == binding.MLA_ERR_INVALID_ARGUMENT
