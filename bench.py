@@ -12,6 +12,7 @@ target is quoted on.  Prints ONE JSON line on stdout; details go to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -104,6 +105,18 @@ def cpu_baseline(inp, seconds: float):
                        % (n, total, dt))
 
 
+def stream_reference_lib():
+    """The benchmark's streaming-read reference kernel, if built."""
+    path = os.path.join(ROOT, "mla_paged_latent_03_amd", "libmla_stream_ref.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mla_stream_read_reference.restype = ctypes.c_int
+    lib.mla_stream_read_reference.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+    return lib
+
+
 def load_traffic(workload: str):
     """HBM bytes per launch of the partial kernel from the rocprofv3 PMC runs
     recorded for this workload, if they were taken on the current sources."""
@@ -121,10 +134,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # The clock settles about 15 ms into a burst of calls (a short fast phase
-    # on a cool GPU, then a dip, then the sustained rate), so the default
-    # warm-up covers that before timing the steady state.
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="run calls for this long before the warm-up, past the clock transient (0: none)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -165,11 +177,10 @@ def main():
         log("[bench] rotating %d input sets (working set below the last-level cache)" % len(sets))
     calls = [0]
 
-    def step(stage1_only=False):
+    def launch(stage1_only):
         o = None if stage1_only else out
         l = None if stage1_only else lse
         inp = sets[calls[0] % len(sets)]
-        calls[0] += 1
         if inp.K > 0 and fp8:
             binding.mla_sparse_decode_fp8(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens,
                                           inp.topk_indices, inp.max_seq_len, inp.softmax_scale, inp.q_scale,
@@ -185,16 +196,25 @@ def main():
             binding.mla_decode(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens,
                                inp.max_seq_len, inp.softmax_scale, o, l, ws, S, stream)
 
-    def timed(n, stage1_only=False):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(n):
-            step(stage1_only)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n           # ms per call
+    def step(ev=None):
+        """One decode call.  With more than one split it is issued as its two
+        stages (first stage, then the merge: the same launches, bit for bit,
+        as one call), so that an event can sit between them; ev = (start,
+        after the first stage, end) events or None."""
+        if ev is not None:
+            ev[0].record(stream)
+        if S > 1:
+            launch(stage1_only=True)
+            if ev is not None:
+                ev[1].record(stream)
+            binding.mla_merge_partials(ws, inp.B * inp.T * inp.H, S, out, lse, stream)
+        else:
+            launch(stage1_only=False)
+            if ev is not None:
+                ev[1].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+        calls[0] += 1
 
     if args.copy_calibration_gib > 0:
         src = torch.ones(args.copy_calibration_gib << 30, dtype=torch.uint8, device=dev)
@@ -205,18 +225,74 @@ def main():
         log("[bench] copied %d GiB three times" % args.copy_calibration_gib)
         del src, dst
 
+    # The GPU clock moves for the first ~15 ms of a burst of decode calls
+    # (fast on an idle GPU, then a dip below the sustained rate, then steady:
+    # power management under full-rate HBM reads plus matrix products).  The
+    # settle phase runs calls until that has passed, so that the warm-up and
+    # timed steps see the sustained rate whatever --warmup is.
+    settle_calls = 0
+    if args.settle_ms > 0:
+        t_end = time.perf_counter() + args.settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                step()
+                settle_calls += 1
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log("[bench] timing %d steps (splits=%d)" % (args.steps, S))
-    ms_step = timed(args.steps)
-    # The dominant (partial) kernel alone: with one split it is the whole call.
-    ms_partial = timed(args.steps, stage1_only=True) if S > 1 else ms_step
+    log("[bench] settled with %d calls, %d warm-up; timing %d steps (splits=%d)"
+        % (settle_calls, args.warmup, args.steps, S))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = evs[0][0].elapsed_time(evs[-1][2]) / args.steps          # whole timed region per step
+    call_us = np.array([e[0].elapsed_time(e[2]) * 1e3 for e in evs])   # per call, partial + merge
+    part_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])   # per call, first stage
+    ms_partial = float(part_us.mean()) * 1e-3
     if not bool(torch.isfinite(out.float()).all()):
         raise RuntimeError("non-finite output")
 
-    # Reference point on the same device: a plain device-to-device copy
-    # (read + write) of 1 GiB, sustained over a few back-to-back copies.
+    def dist(x):
+        return {"median": round(float(np.median(x)), 2), "p10": round(float(np.percentile(x, 10)), 2),
+                "p90": round(float(np.percentile(x, 90)), 2), "mean": round(float(np.mean(x)), 2)}
+
+    # Reference points on the same device.  (1) The streaming-read reference:
+    # the same bytes as the KV cache, read once into LDS through the decode's
+    # DMA path with no arithmetic (libmla_stream_ref.so).  (2) A plain
+    # device-to-device copy (read + write) of 1 GiB.
+    stream_ref = None
+    kv_bytes_all = inp.kv_cache.numel() * inp.kv_cache.element_size()
+    ref_lib = stream_reference_lib()
+    if ref_lib is not None:
+        nbytes = (kv_bytes_all // 36864) * 36864
+        grid = 256
+        sink = torch.empty(grid, dtype=torch.int32, device=dev)
+        def ref_run():
+            rc = ref_lib.mla_stream_read_reference(ctypes.c_void_p(inp.kv_cache.data_ptr()), nbytes, grid,
+                                                   ctypes.c_void_p(sink.data_ptr()),
+                                                   ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError("stream reference failed (%d)" % rc)
+        for _ in range(3):
+            ref_run()
+        torch.cuda.synchronize()
+        r_us = []
+        for _ in range(10):
+            r0 = torch.cuda.Event(enable_timing=True)
+            r1 = torch.cuda.Event(enable_timing=True)
+            r0.record(stream)
+            ref_run()
+            r1.record(stream)
+            torch.cuda.synchronize()
+            r_us.append(r0.elapsed_time(r1) * 1e3)
+        r_med = float(np.median(r_us))
+        stream_ref = {"GBps": round(nbytes / (r_med * 1e-6) / 1e9, 1), "us": round(r_med, 2), "bytes": nbytes,
+                      "kind": "read once into LDS by buffer_load ... lds DMAs (36 KiB tiles, 4-tile ring, "
+                              "256 workgroups of 4 waves), no arithmetic",
+                      "frac_of_peak": round(nbytes / (r_med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
     cdst.copy_(csrc)
@@ -241,12 +317,16 @@ def main():
         achieved = part_bytes / (ms_partial * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4))
+        if stream_ref is not None:
+            roof["frac_of_stream_reference"] = round(achieved / stream_ref["GBps"], 4)
     else:
         achieved = cost["flops"] / (ms_partial * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_PEAK_TFLOPS[kdt], unit="TFLOP/s",
                     frac=round(achieved / MFMA_PEAK_TFLOPS[kdt], 4))
     roof["kernel"] = "mla_partial_kernel"
     roof["us_per_launch"] = round(ms_partial * 1e3, 2)
+    roof["us_per_launch_dist"] = dist(part_us)
+    roof["timed"] = "HIP events around each call's first-stage launch inside the timed calls"
     roof["traffic"] = load_traffic(args.workload)
 
     step_s = ms_step * 1e-3
@@ -272,7 +352,10 @@ def main():
                  "frac_mfma": round(cost["flops"] / step_s / 1e12 / MFMA_PEAK_TFLOPS[kdt], 4),
                  "roofline_frac": round(max(t_hbm, t_mfma) / step_s, 4),
                  "algorithmic_bytes": cost["total_bytes"], "algorithmic_flops": cost["flops"]},
+        "call_us": dist(call_us),
+        "clock_settle": {"ms": args.settle_ms, "calls": settle_calls},
         "roofline": roof,
+        "stream_read_reference": stream_ref,
         "hbm_copy_reference": {"GBps": round(copy_gbps, 1), "kind": "torch copy_ of 1 GiB, read + write bytes",
                                "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},
         "cpu_baseline": None,

@@ -11,6 +11,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
 SOURCES = [os.path.join(CSRC, "mla_decode_kernels.hip"), os.path.join(CSRC, "mla_decode_api.cpp")]
+# Benchmark-only: the streaming-read reference kernel (not part of the decode ABI).
+STREAM_LIB = os.path.join(HERE, "libmla_stream_ref.so")
+STREAM_SRC = os.path.join(CSRC, "stream_ref.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -20,24 +23,22 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", "-Wa
          "-I" + os.path.join(ROOT, "include")]
 
 
-def _device_asm_cmd(out: str):
+def _device_asm_cmd(out: str, src: str):
     flags = [f for f in FLAGS if f not in ("-shared", "-Wall")]
-    return [HIPCC] + flags + ["--offload-device-only", "-S", "-o", out, SOURCES[0]]
+    return [HIPCC] + flags + ["--offload-device-only", "-S", "-o", out, src]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library and, alongside, the kernels' gfx950 assembly; fail
-    if the assembly shows a hazard before an inline-asm memory instruction."""
+def _build_one(lib: str, sources, scanned: str, verbose: bool) -> str:
     from mla_paged_latent_03_amd import asm_hazards
 
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + SOURCES
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-o", tmp] + sources
     if verbose:
         print(" ".join(cmd), flush=True)
     with tempfile.TemporaryDirectory() as td:
         asm_path = os.path.join(td, "kernels.s")
-        asm_proc = subprocess.Popen(_device_asm_cmd(asm_path), stdout=subprocess.DEVNULL, stderr=subprocess.PIPE,
-                                    text=True)
+        asm_proc = subprocess.Popen(_device_asm_cmd(asm_path, scanned), stdout=subprocess.DEVNULL,
+                                    stderr=subprocess.PIPE, text=True)
         res = subprocess.run(cmd, capture_output=True, text=True)
         asm_err = asm_proc.communicate()[1]
         noise = ("packed-fp32-ops", "unknown target feature")
@@ -53,8 +54,16 @@ def build(verbose: bool = False) -> str:
     if found:
         os.remove(tmp)
         raise RuntimeError("hazards before inline-asm memory instructions:\n" + "\n".join(found[:20]))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the decode library and the benchmark's streaming-read
+    reference, each with its kernels' gfx950 assembly alongside; fail if the
+    assembly shows a hazard before an inline-asm memory instruction."""
+    _build_one(STREAM_LIB, [STREAM_SRC], STREAM_SRC, verbose)
+    return _build_one(LIB, SOURCES, SOURCES[0], verbose)
 
 
 if __name__ == "__main__":

@@ -632,7 +632,18 @@ mla_partial_kernel(const PartialParams p) {
     LDS_AS const uint64_t* rows;   // sparse: the tile's token-row addresses
     int n_valid;
   };
-  auto dma_prepare = [&](int i) __attribute__((always_inline)) -> DmaSrc {
+  // Page of tile i (dense; the same LDS word in every lane).  Split from
+  // dma_prepare so that the pipelined steps can read the next step's page
+  // early and build its descriptor late, off the step's critical start.
+  auto dma_page = [&](int i) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) {
+      return 0;
+    } else {
+      const int tok0 = tok_begin + (i < n_tiles ? i : 0) * K::kTileTok;
+      return n_tiles > 0 ? table[(tok0 >> 6) - page0] : -1;
+    }
+  };
+  auto dma_prepare_pg = [&](int i, int pg_v) __attribute__((always_inline)) -> DmaSrc {
     DmaSrc d;
     const bool real = i < n_tiles;
     if (SPARSE) {
@@ -641,9 +652,9 @@ mla_partial_kernel(const PartialParams p) {
       d.n_valid = real ? K::kTileTok : 0;
     } else {
       const int tok0 = tok_begin + (real ? i : 0) * K::kTileTok;
-      // Same address in every lane; taken into a scalar register at once so
-      // that the descriptor arithmetic below stays on the scalar unit.
-      const int pg = n_tiles > 0 ? __builtin_amdgcn_readfirstlane(table[(tok0 >> 6) - page0]) : -1;
+      // Taken into a scalar register at once so that the descriptor
+      // arithmetic below stays on the scalar unit.
+      const int pg = n_tiles > 0 ? __builtin_amdgcn_readfirstlane(pg_v) : -1;
       const int n_valid = (real && pg >= 0) ? min(K::kTileTok, L - tok0) : 0;
       d.rsrc = buffer_rsrc(p.kv + ((int64_t)(pg >= 0 ? pg : 0) * 64 + (tok0 & 63)) * K::kRowBytes,
                            (uint32_t)(n_valid * K::kRowBytes));
@@ -652,6 +663,7 @@ mla_partial_kernel(const PartialParams p) {
     }
     return d;
   };
+  auto dma_prepare = [&](int i) __attribute__((always_inline)) -> DmaSrc { return dma_prepare_pg(i, dma_page(i)); };
   // DMA instruction j of a tile into ring slot `slot`.
   auto dma_issue = [&](const DmaSrc& d, int slot, int j) __attribute__((always_inline)) {
     const uint32_t dst = lds_u32 + slot * kTileBytes + (wave * NI + j) * 1024;
@@ -1075,8 +1087,8 @@ mla_partial_kernel(const PartialParams p) {
   // (token block 0, then block 1) with the DMA of tile i+NS-1 spread between
   // its products and token block 0's softmax between block 1's products;
   // then the PV products of tile i with block 1's softmax between them.
-  auto pipe_step = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped, auto mask_c,
-                       auto resid_c) __attribute__((always_inline)) {
+  auto pipe_step = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped, DmaSrc& src, int& pg_nx,
+                       auto mask_c, auto resid_c) __attribute__((always_inline)) {
     constexpr bool mask = decltype(mask_c)::value;
     constexpr int KS = K::kQkSteps;
     // Tile i+1 resident (one tile may still be in flight behind it); every
@@ -1085,8 +1097,7 @@ mla_partial_kernel(const PartialParams p) {
     lds_barrier();
     const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
     const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
-    const int nxt = i + NS - 1;                  // past the end: a zero fill of a free slot
-    const DmaSrc src = dma_prepare(nxt);
+    const int nxt = i + NS - 1;   // past the end: a zero fill of a free slot; src covers it
     constexpr int DSTRIDE = NQK / NI;
     static_assert(NQK % NI == 0, "DMA spread");
     opnd_t qa[3], va[3];
@@ -1104,6 +1115,7 @@ mla_partial_kernel(const PartialParams p) {
       if (n == KS) mfma_drain(sacc[0]);          // block 0's chain ended one product ago
       if (n > KS) sm_block_stage(n - KS - 1, mask, sacc, i + 1, 0, jumped, st, pn, resid_c);
       if (n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
+      if (n == 1) pg_nx = dma_page(nxt + 1);     // consumed at the end of the step
       __builtin_amdgcn_sched_barrier(0);
     }
     static_assert(NSTAGE_BLOCK + 1 <= KS - 1, "block 0's stages fit between block 1's products");
@@ -1119,6 +1131,7 @@ mla_partial_kernel(const PartialParams p) {
     }
     static_assert(NSTAGE_BLOCK + 3 <= NPV, "block 1's stages fit between the PV products");
     row_sum_mfma(pt, resid_c);
+    src = dma_prepare_pg(nxt + 1, pg_nx);        // the next step's DMA source
     pt = pn;
   };
 
@@ -1184,8 +1197,8 @@ mla_partial_kernel(const PartialParams p) {
   // tile i's softmax state and P tile with all but block 1's last four
   // exponent stages and the finish done, and sacc[1] holds tile i's block-1
   // scores; leaving, the same holds for tile i+1.
-  auto pipe_step_fs = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, SmState& st, bool& jumped,
-                          auto mask_c) __attribute__((always_inline)) {
+  auto pipe_step_fs = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, SmState& st, bool& jumped, DmaSrc& src,
+                          int& pg_nx, auto mask_c) __attribute__((always_inline)) {
     constexpr bool mask = decltype(mask_c)::value;     // tile i+1's softmax takes the mask
     constexpr int HEAD = FS_NSTAGE - 4 + (mask ? 1 : 0);   // stages before the last four exponent stages
     constexpr int KS = K::kQkSteps;
@@ -1194,8 +1207,7 @@ mla_partial_kernel(const PartialParams p) {
     lds_barrier();     // tile i+1 resident; slot i-1 free; every wave done with tile i-1's P tiles
     const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
     const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
-    const int nxt = i + NS - 1;
-    const DmaSrc src = dma_prepare(nxt);
+    const int nxt = i + NS - 1;   // src (built by the previous step) covers this tile
     opnd_t qa[3];
     qa[0] = ld_qk(tq, 0);
     qa[1] = ld_qk(tq, 1);
@@ -1229,6 +1241,7 @@ mla_partial_kernel(const PartialParams p) {
       if (b == 0) mfma_drain(sacc[0]);           // block 0's chain ended one product ago
       if (b >= 1 && b - 1 < HEAD) fs_stage(b - 1, mask, sacc, i + 1, 0, jumped, sn, pn);
       if (b % 2 == 0) dma_issue(src, nxt % NS, 4 + b / 2);
+      if (b == 1) pg_nx = dma_page(nxt + 1);     // consumed at the end of phase C
       __builtin_amdgcn_sched_barrier(0);
     }
     static_assert(FS_NSTAGE - 4 + 1 <= KS - 1, "block 0's first stages fit phase B");
@@ -1252,6 +1265,7 @@ mla_partial_kernel(const PartialParams p) {
     }
     static_assert(FS_NSTAGE - 4 + 1 <= 8, "block 1's first stages fit phase C");
     row_sum_mfma(pt, std::false_type{});
+    src = dma_prepare_pg(nxt + 1, pg_nx);        // the next step's DMA source
     pt = pn;
     st = sn;
   };
@@ -1260,16 +1274,15 @@ mla_partial_kernel(const PartialParams p) {
   // with the DMA of tile i+NS-1 spread between its products, then the 32 PV
   // products of tile i with the softmax stages of tile i+1 between them.
   // Operands are loaded QD products ahead.
-  auto pipe_step_bf16 = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped,
-                            auto mask_c) __attribute__((always_inline)) {
+  auto pipe_step_bf16 = [&](int i, f32x16_t (&sacc)[K::kTokBlocks], PTile& pt, bool& jumped, DmaSrc& src,
+                            int& pg_nx, auto mask_c) __attribute__((always_inline)) {
     constexpr bool mask = decltype(mask_c)::value;
     constexpr int QD = 2;
     wait_vmcnt<NI * (NS - 3)>();
     lds_barrier();
     const LDS_AS uint8_t* tv = lds + (i % NS) * kTileBytes;
     const LDS_AS uint8_t* tq = lds + ((i + 1) % NS) * kTileBytes;
-    const int nxt = i + NS - 1;
-    const DmaSrc src = dma_prepare(nxt);
+    const int nxt = i + NS - 1;   // src covers this tile
     constexpr int DSTRIDE = NQK / NI;
     static_assert(NQK % NI == 0, "DMA spread");
     opnd_t qa[QD + 1], va[QD + 1];
@@ -1282,6 +1295,7 @@ mla_partial_kernel(const PartialParams p) {
       __builtin_amdgcn_sched_barrier(0);
       qk_mfma(sacc, n, qa[n % (QD + 1)]);
       if (n % DSTRIDE == DSTRIDE - 1) dma_issue(src, nxt % NS, n / DSTRIDE);
+      if (n == 1) pg_nx = dma_page(nxt + 1);     // consumed at the end of the step
       __builtin_amdgcn_sched_barrier(0);
     }
     PTile pn;
@@ -1300,6 +1314,7 @@ mla_partial_kernel(const PartialParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     static_assert(3 * (NSTAGE_BLOCK + 1) + 1 < NPV, "the bf16 softmax stages fit between the PV products");
+    src = dma_prepare_pg(nxt + 1, pg_nx);        // the next step's DMA source
     pt = pn;
   };
 
@@ -1344,8 +1359,10 @@ mla_partial_kernel(const PartialParams p) {
 #pragma unroll
             for (int k = 0; k < FS_NSTAGE + 1 - (tb == 1 ? 4 : 0); k++)
               fs_stage(k, true, sacc, 0, tb, jumped, st, pt);
-          for (; i + 1 < n_clean; i++) pipe_step_fs(i, sacc, pt, st, jumped, clean_t{});
-          for (; i + 1 < n_tiles; i++) pipe_step_fs(i, sacc, pt, st, jumped, masked_t{});
+          DmaSrc src = dma_prepare(NS - 1);
+          int pg_nx = 0;
+          for (; i + 1 < n_clean; i++) pipe_step_fs(i, sacc, pt, st, jumped, src, pg_nx, clean_t{});
+          for (; i + 1 < n_tiles; i++) pipe_step_fs(i, sacc, pt, st, jumped, src, pg_nx, masked_t{});
           // Last tile: the rest of its softmax, publish, PV.
 #pragma unroll
           for (int d = 4; d < FS_NEXP; d++) fs_exp(sacc, 1, d, st, pt);
@@ -1353,12 +1370,14 @@ mla_partial_kernel(const PartialParams p) {
           fs_write_p(pt);
         } else {
           softmax_all(sacc, 0, jumped, pt, resid_c);
+          DmaSrc src = dma_prepare(NS - 1);
+          int pg_nx = 0;
           if constexpr (FP8) {
-            for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, clean_t{}, resid_c);
-            for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, masked_t{}, resid_c);
+            for (; i + 1 < n_clean; i++) pipe_step(i, sacc, pt, jumped, src, pg_nx, clean_t{}, resid_c);
+            for (; i + 1 < n_tiles; i++) pipe_step(i, sacc, pt, jumped, src, pg_nx, masked_t{}, resid_c);
           } else {
-            for (; i + 1 < n_clean; i++) pipe_step_bf16(i, sacc, pt, jumped, clean_t{});
-            for (; i + 1 < n_tiles; i++) pipe_step_bf16(i, sacc, pt, jumped, masked_t{});
+            for (; i + 1 < n_clean; i++) pipe_step_bf16(i, sacc, pt, jumped, src, pg_nx, clean_t{});
+            for (; i + 1 < n_tiles; i++) pipe_step_bf16(i, sacc, pt, jumped, src, pg_nx, masked_t{});
           }
         }
 
@@ -1396,10 +1415,13 @@ mla_partial_kernel(const PartialParams p) {
       // one tile in flight at a time).  Past the end the slot gets a zero
       // fill, which keeps the wait a constant.
       static_assert(NS == 2, "two-slot loop");
+      // The DMA source of the next tile is built at the end of the previous
+      // iteration from a page read early in it, off the iteration's start.
+      DmaSrc src = dma_prepare(1);
+      int pg_nx = 0;
       for (int i = 0; i < n_tiles; i++) {
         wait_vmcnt<0>();
         if (RG > 1) lds_barrier();   // tile i complete; every wave is done with tile i-1's slot
-        const DmaSrc src = dma_prepare(i + 1);
         const LDS_AS uint8_t* tile = lds + (i % NS) * kTileBytes;
         f32x16_t sacc[K::kTokBlocks];
         {
@@ -1419,6 +1441,7 @@ mla_partial_kernel(const PartialParams p) {
 #pragma unroll
               for (int j = 0; j < NI; j++) dma_issue(src, (i + 1) % NS, j);
             }
+            if (n == 1) pg_nx = dma_page(i + 2);
             __builtin_amdgcn_sched_barrier(0);
           }
           drain_scores(sacc);
@@ -1436,6 +1459,7 @@ mla_partial_kernel(const PartialParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
         row_sum_mfma(pt, resid_c);
+        src = dma_prepare_pg(i + 2, pg_nx);
       }
       wait_vmcnt<0>();   // the zero fill past the end must land before the LDS is reused
     }
