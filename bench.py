@@ -139,6 +139,8 @@ def main():
                     help="run calls for this long before the warm-up, past the clock transient (0: none)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's choice")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="request the single-launch form (MLA_SINGLE_LAUNCH=1): split units merge in-kernel")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-gib", type=int, default=0,
@@ -151,6 +153,10 @@ def main():
               "(its sequence-sharded multi-GPU form is not implemented). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.single_launch:
+        os.environ["MLA_SINGLE_LAUNCH"] = "1"
+    else:
+        os.environ.pop("MLA_SINGLE_LAUNCH", None)
     import torch
     from mla_paged_latent_03_amd import binding, workloads as wl
 
@@ -164,6 +170,8 @@ def main():
                       dtype=torch.float32 if inp.out_dtype == "f32" else torch.bfloat16)
     lse = torch.empty((inp.B, inp.T, inp.H), device=dev, dtype=torch.float32)
     ws_bytes = binding.workspace_size(inp.B, inp.T, inp.H, inp.max_seq_len, inp.K, fp8, S)
+    partial_bytes = inp.B * inp.T * inp.H * S * 513 * 4 if S > 1 else 0
+    single = ws_bytes > partial_bytes          # the plan adds the group words of the single-launch form
     ws = torch.empty(max(1, (ws_bytes + 3) // 4), device=dev, dtype=torch.float32) if ws_bytes else None
     stream = torch.cuda.current_stream()
 
@@ -203,7 +211,7 @@ def main():
         after the first stage, end) events or None."""
         if ev is not None:
             ev[0].record(stream)
-        if S > 1:
+        if S > 1 and not single:
             launch(stage1_only=True)
             if ev is not None:
                 ev[1].record(stream)
@@ -345,7 +353,7 @@ def main():
         "data": "synthetic (seeded N(0,1) values, shuffled pages)",
         "config": {"workload": args.workload, "batch": inp.B, "heads": inp.H, "q_len": inp.T,
                    "max_seq_len": inp.max_seq_len, "block_size": 64, "topk": inp.K, "kv_splits": S,
-                   "out_dtype": inp.out_dtype},
+                   "out_dtype": inp.out_dtype, "launches": "one" if (single or S == 1) else "two"},
         "step": {"hbm_TBps": round(cost["total_bytes"] / step_s / 1e12, 3),
                  "mfma_TFLOPs": round(cost["flops"] / step_s / 1e12, 1),
                  "frac_hbm": round(cost["total_bytes"] / step_s / 1e12 / (HBM_PEAK_GBPS / 1e3), 4),

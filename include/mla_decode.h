@@ -51,6 +51,17 @@
  * rounds and numbers the pieces longest first.  Other calls cut fixed chunks of
  * ceil(ceil(max_seq_len / 64) / splits) pages.  Either way the merged result
  * is the same attention; rounding differs with the cut.
+ *   Single launch (tokenspeed's in-kernel merge, vLLM PR #41778 digest,
+ * "Implementation" item 1): with the environment variable
+ * MLA_SINGLE_LAUNCH=1, a call whose units all fit the device at once (one
+ * round of workgroups, at most 64 splits) runs as one kernel: the units of
+ * each (sequence, row block) meet at two 8-byte words after the partials
+ * and merge the block's rows themselves, with the same arithmetic and
+ * result bits as the merge kernel.  The words carry the call's number and
+ * need no clearing; they are left at zero counts, so graph replays work.
+ * On MI355X it measures slower than the two launches (the units share no
+ * L2, so their meeting costs device-scope round trips), so it is off by
+ * default.
  *
  * Conventions shared by every entry point:
  *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
@@ -150,7 +161,8 @@ int mla_launch_waves(int batch, int q_len, int num_heads, int max_seq_len, int t
 
 /*
  * Workspace bytes a call needs: batch * q_len * num_heads * splits * 513 * 4,
- * or 0 when the call runs with one split.  num_kv_splits = 0 means the
+ * or 0 when the call runs with one split; with the single launch (below)
+ * rounded up to 16 and followed by 16 bytes per (sequence, row block).  num_kv_splits = 0 means the
  * heuristic choice above.  Returns 0 for invalid arguments as well; pass the
  * same arguments to the decode call.
  */

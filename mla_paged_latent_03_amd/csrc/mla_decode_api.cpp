@@ -5,14 +5,16 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <mutex>
 
 #include "mla_decode_internal.h"
 
 namespace {
 
-using mla::kNumCUs;
 using mla::kPartialWidth;
 using mla::kDensePagesMax;
 using mla::kSparseChunkMax;
@@ -30,16 +32,60 @@ struct Plan {
   int max_pages = 0;      // dense: pages of max_seq_len
   int unit_pages = 0;     // dense: a work unit's pages when every sequence is max_seq_len long
   int64_t grid_units = 0; // work units the launch covers
+  bool fused = false;     // one launch: the units merge their partials themselves
+  int64_t groups = 0;     // (sequence, row block) groups that merge together
   size_t ws_bytes = 0;
 };
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// The single-launch form (the split units merge their partials themselves)
+// is chosen only when the environment variable MLA_SINGLE_LAUNCH is "1".
+// Measured against the two launches it is slower on every workload here:
+// its units live on different XCDs, whose L2 caches are not coherent, so
+// the partials go through device-scope stores and loads and the units meet
+// at device-scope atomics, several round trips of a few microseconds each,
+// more than the merge kernel and the launch gap it saves.  Read on every
+// plan, so the sizing queries and the decode call agree within a process
+// that does not change it in between.
+bool single_launch_requested() {
+  const char* v = std::getenv("MLA_SINGLE_LAUNCH");
+  return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+// Compute units of the current device, looked up once per device and
+// cached (the library's only cache).  A partitioned MI355X or a CU-masked
+// process shows fewer, and every plan follows what the device reports.
+// Without a usable device (host-only queries) the MI355X's 256 are assumed.
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int cached[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return mla::kDefaultCUs;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      n = mla::kDefaultCUs;
+    }
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 int rg_for_rows(int rows) { return rows <= 32 ? 1 : (rows <= 64 ? 2 : 4); }
 
-// Resident workgroups per CU for a row-group width (LDS ring: 4 x 36 KiB for
-// 4 waves, 2 x 36 KiB otherwise).
-int wg_per_cu(int rg) { return rg == 4 ? 1 : 2; }
+// Resident workgroups per CU for a row-group width, from the LDS each
+// variant takes out of the CU's 160 KiB: four waves ring 4 x 36 KiB (one
+// workgroup); one or two waves ring 2 x 36 KiB plus their table (two
+// workgroups dense, where the page table is 4 KiB; one sparse, where the
+// 8-byte row addresses of 1024 indices make it 82 KiB).
+int wg_per_cu(int rg, bool sparse) { return rg == 4 || sparse ? 1 : 2; }
 
 bool dims_ok(int B, int T, int H, int max_seq_len, int topk) {
   return B >= 0 && B <= (1 << 20) && T >= 1 && T <= MLA_MAX_Q_LEN && H >= 1 && H <= 1024 &&
@@ -67,6 +113,7 @@ int balanced_length(int B, int n_pages, int S, int n_target) {
 // The cheapest candidate wins; ties go to fewer splits, then wider blocks.
 bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req_splits, Plan* pl) {
   if (!dims_ok(B, T, H, max_seq_len, topk) || req_splits < 0 || req_splits > MLA_MAX_KV_SPLITS) return false;
+  const int n_cu = device_cu_count();
   Plan p;
   p.R = T * H;
   const bool sparse = topk > 0;
@@ -95,7 +142,7 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
   double best = -1.0;
   for (int g = g_first; g >= 1; g >>= 1) {
     const int64_t n_blk = ceil_div(rows_blk, 32 * g);
-    const int64_t slots = (int64_t)kNumCUs * wg_per_cu(g);
+    const int64_t slots = (int64_t)n_cu * wg_per_cu(g, sparse);
     for (int s = s_min < 1 ? 1 : s_min; s <= (s_max > s_min ? s_max : s_min); s++) {
       const int64_t units = lists * n_blk * s;
       if (units <= 0) break;
@@ -134,7 +181,7 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
     // above assumes every sequence is max_seq_len long; in a mixed batch a
     // long sequence may need more pieces than that, so the library's own
     // choice gives each sequence twice the slots.
-    const int64_t slots = (int64_t)kNumCUs * wg_per_cu(rg);
+    const int64_t slots = (int64_t)n_cu * wg_per_cu(rg, sparse);
     const int n_target = (int)std::max<int64_t>(1, slots / p.n_rb);
     p.balance = S > 1 && B <= mla::kBalanceMaxBatch && B < n_target;
     if (p.balance && req_splits == 0) S = std::max(S, std::min(2 * S, s_max));
@@ -171,8 +218,30 @@ bool make_plan(int B, int T, int H, int max_seq_len, int topk, bool fp8, int req
   }
   p.S = S;
   p.ws_bytes = S > 1 ? (size_t)B * p.R * S * kPartialWidth * sizeof(float) : 0;
+  // Single launch (opt-in, single_launch_requested): when every unit of the
+  // launch is resident at once (one round of workgroup slots), the units of
+  // each (sequence, row block) wait for each other and merge the block's
+  // rows themselves, so there is no second kernel and no launch gap.  Two
+  // 8-byte words per group follow the partials in the workspace.
+  const int64_t launched = (p.grid_units + 7) / 8 * 8;
+  p.groups = (int64_t)B * p.n_rb;
+  // Residency is what the runtime reports for the variant (the LDS model
+  // above when it cannot be asked): the single launch waits on it.
+  const bool resid_kernel = fp8 && (sparse || (int64_t)p.unit_pages * MLA_BLOCK_SIZE <= mla::kFp8ResidualMaxUnitTokens);
+  const int occ = mla::partial_kernel_occupancy(fp8, sparse, p.rg, resid_kernel);
+  const int64_t resident = (int64_t)n_cu * (occ > 0 ? occ : wg_per_cu(p.rg, sparse));
+  p.fused = single_launch_requested() && S > 1 && S <= 64 && launched <= resident;
+  if (p.fused) p.ws_bytes = (p.ws_bytes + 15) / 16 * 16 + (size_t)p.groups * 16;
   *pl = p;
   return true;
+}
+
+// Number of this call among the library's calls in this process (48 bits);
+// marks the group words of a single-launch call, so that words left by an
+// earlier call (or never written) count as zero and need no clearing.
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> counter{1};
+  return counter.fetch_add(1, std::memory_order_relaxed) & ((1ull << 48) - 1);
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
@@ -242,6 +311,11 @@ mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv
   p.out_f32 = out_dtype == MLA_OUT_F32;
   p.lse = lse;
   p.ws = pl.S > 1 ? (float*)workspace : nullptr;
+  p.fused = pl.fused && !stage1_only ? 1 : 0;
+  p.sync = p.fused ? (unsigned long long*)((uint8_t*)workspace +
+                                           ((size_t)B * pl.R * pl.S * kPartialWidth * sizeof(float) + 15) / 16 * 16)
+                   : nullptr;
+  p.epoch = p.fused ? next_epoch() : 0;
   const int grid = (int)((units + 7) / 8 * 8);
   hipStream_t st = (hipStream_t)stream;
   // fp8: units planned at most kFp8ResidualMaxUnitTokens long take the
@@ -251,7 +325,7 @@ mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv
   const int64_t unit_tokens = (int64_t)(sparse ? pl.chunk : pl.unit_pages * MLA_BLOCK_SIZE);
   const bool resid = fp8 && unit_tokens <= mla::kFp8ResidualMaxUnitTokens;
   if (mla::launch_partial_kernel(p, fp8, sparse, pl.rg, resid, grid, st) != hipSuccess) return MLA_ERR_HIP;
-  if (pl.S > 1 && !stage1_only) {
+  if (pl.S > 1 && !stage1_only && !p.fused) {
     mla::MergeParams m{};
     m.ws = (const float*)workspace;
     m.n_rows = (int64_t)B * pl.R;

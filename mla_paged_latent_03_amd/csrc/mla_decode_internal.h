@@ -12,7 +12,7 @@ constexpr int kPage = 64;
 constexpr int kPartialWidth = kLatentDim + 1;   // normalized outputs, then the chunk's lse
 constexpr int kSparseChunkMax = 1024;           // top-k entries one workgroup handles
 constexpr int kDensePagesMax = 1024;            // pages one workgroup handles (65536 tokens)
-constexpr int kNumCUs = 256;                    // MI355X compute units
+constexpr int kDefaultCUs = 256;                // MI355X compute units (when no device can be asked)
 constexpr int kBalanceMaxBatch = 1024;          // largest batch whose split lengths are balanced on the device
 
 struct PartialParams {
@@ -38,6 +38,13 @@ struct PartialParams {
   int out_f32;
   float* lse;                   // [B, T, H] or null (one split)
   float* ws;                    // [B, R, S, 513] (more than one split)
+  // Single launch (more than one split, every unit resident at once): the
+  // units of a (sequence, row block) meet at two words of `sync` and then
+  // merge the group's rows themselves.  sync: [groups][2] words of
+  // (epoch << 16 | count); epoch: this call's number (48 bits).
+  unsigned long long* sync;
+  unsigned long long epoch;
+  int fused;
 };
 
 struct MergeParams {
@@ -61,6 +68,11 @@ constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
 
 // Device address of this GPU's static workspace (looked up once per device).
 hipError_t static_scratch(void** ptr);
+
+// Workgroups of the partial-kernel variant (fp8, sparse, waves, residual
+// product) that one compute unit of the current device holds at once, as
+// the runtime reports it; 0 when it cannot be asked.
+int partial_kernel_occupancy(bool fp8, bool sparse, int rg, bool resid);
 
 hipError_t launch_partial_kernel(const PartialParams& p, bool fp8, bool sparse, int rg, bool resid, int grid,
                                  hipStream_t stream);

@@ -409,6 +409,109 @@ __device__ __attribute__((always_inline)) inline bool balanced_piece(const Parti
   return balanced_piece_m<kBalanceMaxBatch / 64>(p, j, pc);
 }
 
+// A device-scope load: reads what other XCDs wrote with device-scope stores,
+// whatever this XCD's L2 held.
+__device__ inline float coherent_load(const float* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// LSE merge of NR rows by one wave (lane l: outputs 8l .. 8l+7), all rows'
+// loads issued before any is used; at most 64 splits.  The arithmetic of
+// each row is that of mla_merge_kernel, so both give the same bits.
+template <int NR>
+__device__ __attribute__((always_inline)) inline void merge_rows(const float* ws, const int64_t (&rows)[NR],
+                                                                 const bool (&valid)[NR], int S, void* out,
+                                                                 int out_f32, float* lse) {
+  const int lane = threadIdx.x & 63;
+  float mx[NR], w[NR], z[NR];
+#pragma unroll
+  for (int i = 0; i < NR; i++)
+    mx[i] = (valid[i] && lane < S) ? coherent_load(ws + (rows[i] * S + lane) * (int64_t)kPartialWidth + 512)
+                                    : -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NR; i++) {
+    w[i] = mx[i];    // this lane's split lse
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], d));
+  }
+#pragma unroll
+  for (int i = 0; i < NR; i++) {
+    w[i] = (mx[i] != -INFINITY && lane < S) ? __expf(w[i] - mx[i]) : 0.f;
+    float zs = w[i];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) zs += __shfl_xor(zs, d);
+    z[i] = 0.f + zs;
+  }
+  float acc[NR][8];
+#pragma unroll
+  for (int i = 0; i < NR; i++)
+#pragma unroll
+    for (int c = 0; c < 8; c++) acc[i][c] = 0.f;
+  for (int k0 = 0; k0 < S; k0 += 8) {
+    float wk[NR][8];
+    float v[NR][8][8];
+#pragma unroll
+    for (int i = 0; i < NR; i++)
+#pragma unroll
+      for (int k = 0; k < 8; k++) wk[i][k] = __shfl(w[i], (k0 + k) & 63);   // 0 past S
+#pragma unroll
+    for (int i = 0; i < NR; i++)
+#pragma unroll
+      for (int k = 0; k < 8; k++)
+        if (wk[i][k] != 0.f) {
+          const float* src = ws + (rows[i] * S + k0 + k) * (int64_t)kPartialWidth + 8 * lane;
+#pragma unroll
+          for (int c = 0; c < 8; c++) v[i][k][c] = coherent_load(src + c);
+        }
+#pragma unroll
+    for (int i = 0; i < NR; i++)
+#pragma unroll
+      for (int k = 0; k < 8; k++)
+        if (wk[i][k] != 0.f) {
+#pragma unroll
+          for (int c = 0; c < 8; c++) acc[i][c] += wk[i][k] * v[i][k][c];
+        }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; i++) {
+    if (!valid[i]) continue;
+    float lse_out = -INFINITY;
+    if (mx[i] != -INFINITY) {
+      const float inv = 1.f / z[i];
+#pragma unroll
+      for (int c = 0; c < 8; c++) acc[i][c] *= inv;
+      lse_out = mx[i] + __logf(z[i]);
+    }
+    if (out_f32) {
+      float* o = (float*)out + rows[i] * 512 + 8 * lane;
+      *(float4*)o = float4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+      *(float4*)(o + 4) = float4{acc[i][4], acc[i][5], acc[i][6], acc[i][7]};
+    } else {
+      typedef __bf16 bf16x8s_t __attribute__((ext_vector_type(8)));
+      bf16x8s_t bv;
+#pragma unroll
+      for (int c = 0; c < 8; c++) bv[c] = (__bf16)acc[i][c];
+      *(bf16x8s_t*)((__bf16*)out + rows[i] * 512 + 8 * lane) = bv;
+    }
+    if (lane == 0 && lse) lse[rows[i]] = lse_out;
+  }
+}
+
+// Arrival at a group word (epoch << 16 | count): a word of another epoch
+// counts as zero.  Returns the count after this arrival, or 0 if the word
+// could not be updated within the bound.
+__device__ inline int sync_arrive(unsigned long long* word, unsigned long long e) {
+  unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0; it < (1 << 20); it++) {
+    const unsigned long long base = (cur >> 16) == (e >> 16) ? cur : e;
+    if (__hip_atomic_compare_exchange_strong(word, &cur, base + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return (int)((base + 1) & 0xffff);
+  }
+  return 0;
+}
+
 // ---------------------------------------------------------------------------
 // Split-KV partial kernel.
 //   FP8    : e4m3 cache and query (else bf16)
@@ -1635,6 +1738,14 @@ mla_partial_kernel(const PartialParams p) {
 
   // This lane's 16 values of output feature block fb of query row qr (the
   // C layout: register 4a+c holds feature 32 fb + 8a + 4h + c).
+  // A float of a split partial.  A single-launch call writes its partials
+  // with device-scope stores (through to the device's coherence point), so
+  // that the units merging them on other XCDs read them without any cache
+  // write-back or invalidation.
+  auto put = [&](float* a, float v) __attribute__((always_inline)) {
+    if (p.fused) __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *a = v;
+  };
   auto store_block = [&](int64_t qr, int fb, const f32x16_t& acc, float iv) {
     if (p.S == 1) {
       if (p.out_f32) {
@@ -1659,7 +1770,7 @@ mla_partial_kernel(const PartialParams p) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; a4++)
 #pragma unroll
-        for (int c = 0; c < 4; c++) w[8 * a4 + c] = acc[4 * a4 + c] * iv;
+        for (int c = 0; c < 4; c++) put(&w[8 * a4 + c], acc[4 * a4 + c] * iv);
     }
   };
   // Split partials of four-wave blocks leave through LDS.  In the
@@ -1696,8 +1807,8 @@ mla_partial_kernel(const PartialParams p) {
       for (int k = 0; k < 8; k++) {
         if ((ok >> (r0 + k)) & 1u) {
           float* w = p.ws + ((qr0 + r0 + k) * p.S + split) * (int64_t)kPartialWidth + fbase;
-          w[lane] = v[2 * k];
-          w[64 + lane] = v[2 * k + 1];
+          put(&w[lane], v[2 * k]);
+          put(&w[64 + lane], v[2 * k + 1]);
         }
       }
     }
@@ -1708,12 +1819,12 @@ mla_partial_kernel(const PartialParams p) {
       if (p.lse) p.lse[qrow] = lse_v;
     } else {
       float* wl = p.ws + qrow * p.S * (int64_t)kPartialWidth + 512;
-      wl[split * (int64_t)kPartialWidth] = lse_v;
+      put(&wl[split * (int64_t)kPartialWidth], lse_v);
       // A sequence cut into fewer pieces than it has slots: its last piece
       // marks the remaining slots empty (lse -inf; their outputs are left
       // unwritten and the merge does not read them).
       if (split == n_split - 1)
-        for (int s = n_split; s < p.S; s++) wl[s * (int64_t)kPartialWidth] = -INFINITY;
+        for (int s = n_split; s < p.S; s++) put(&wl[s * (int64_t)kPartialWidth], -INFINITY);
     }
   };
 
@@ -1753,14 +1864,56 @@ mla_partial_kernel(const PartialParams p) {
       const int64_t qr0 = qrow - l32;
 #pragma unroll
       for (int c = 0; c < 4; c++) stage_partial(&oacc[4 * c], qr0, 128 * c, inv, ok);
-      if (!row_ok) return;
       store_lse();
-      return;
-    }
-    if (!row_ok) return;
+    } else if (row_ok) {
 #pragma unroll
-    for (int fb = 0; fb < 16; fb++) store_block(qrow, fb, oacc[fb], inv);
-    store_lse();
+      for (int fb = 0; fb < 16; fb++) store_block(qrow, fb, oacc[fb], inv);
+      store_lse();
+    }
+  }
+
+  // ---- single launch: the units of this (sequence, row block) wait for
+  // each other, then each merges its share of the block's rows.  Every unit
+  // of the launch is resident at once (the host plans this form only then),
+  // so the wait ends; it is bounded all the same.
+  if (p.fused && p.S > 1) {
+    unsigned long long* word = p.sync + 2 * ((int64_t)b * p.n_rb + rb);
+    const unsigned long long e = p.epoch << 16;
+    wait_vmcnt<0>();            // this wave's partial stores have reached the device
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      sync_arrive(word, e);
+      // Device-scope reads of the word; the partials are read the same way,
+      // so no fence (an L2 write-back or invalidation) is needed anywhere.
+      for (int it = 0; it < (1 << 22); it++) {
+        if (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (e | (unsigned)n_split)) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    // Rows of the block: dense rb covers rows [32 RG rb, ...) of the
+    // sequence; sparse rb is (draft token, head block).
+    int row0, nrows;
+    if (SPARSE) {
+      const int hb = rb % p.n_hb;
+      row0 = (rb / p.n_hb) * p.H + hb * (32 * RG);
+      nrows = min(32 * RG, p.H - hb * (32 * RG));
+    } else {
+      row0 = rb * (32 * RG);
+      nrows = min(32 * RG, p.R - row0);
+    }
+    const int r_beg = split * nrows / n_split, r_end = (split + 1) * nrows / n_split;
+    for (int r = r_beg + wave; r < r_end; r += 2 * RG) {
+      const int64_t rows2[2] = {(int64_t)b * p.R + row0 + r, (int64_t)b * p.R + row0 + r + RG};
+      const bool ok2[2] = {true, r + RG < r_end};
+      merge_rows<2>(p.ws, rows2, ok2, p.S, p.out, p.out_f32, p.lse);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && sync_arrive(word + 1, e) == n_split) {
+      // every unit of the group is past its wait: both words back to zero
+      __hip_atomic_store(word, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(word + 1, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -1881,6 +2034,54 @@ hipError_t launch_partial_kernel(const PartialParams& p, bool fp8, bool sparse, 
     }
   }
   return hipErrorInvalidValue;
+}
+
+// Workgroups of a partial-kernel variant that one compute unit holds at
+// once, as the runtime reports it for the current device (cached per
+// device and variant); 0 if it cannot be asked.
+template <bool FP8, bool SPARSE, int RG, int NS, bool RESID = false, bool FS = false>
+static int occupancy_of() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mla_partial_kernel<FP8, SPARSE, RG, NS, RESID, FS>, 64 * RG,
+                                                   0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+int partial_kernel_occupancy(bool fp8, bool sparse, int rg, bool resid) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int cached[kMaxDevices][2][2][3][2] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int gi = rg == 4 ? 2 : rg - 1;
+  std::lock_guard<std::mutex> lock(mu);
+  int& c = cached[dev][fp8][sparse][gi][resid];
+  if (c == 0) {
+    int n = 0;
+    if (fp8 && !sparse) {
+      if (resid) n = rg == 1 ? occupancy_of<true, false, 1, 2, true>() : rg == 2 ? occupancy_of<true, false, 2, 2, true>()
+                                                                         : occupancy_of<true, false, 4, 4, true>();
+      else n = rg == 1 ? occupancy_of<true, false, 1, 2>() : rg == 2 ? occupancy_of<true, false, 2, 2>()
+                                                           : occupancy_of<true, false, 4, 4, false, true>();
+    } else if (!fp8 && !sparse) {
+      n = rg == 1 ? occupancy_of<false, false, 1, 2>() : rg == 2 ? occupancy_of<false, false, 2, 2>()
+                                                       : occupancy_of<false, false, 4, 4>();
+    } else if (!fp8 && sparse) {
+      n = rg == 1 ? occupancy_of<false, true, 1, 2>() : rg == 2 ? occupancy_of<false, true, 2, 2>()
+                                                      : occupancy_of<false, true, 4, 4>();
+    } else {
+      n = rg == 1 ? occupancy_of<true, true, 1, 2, true>() : rg == 2 ? occupancy_of<true, true, 2, 2, true>()
+                                                           : occupancy_of<true, true, 4, 4, true>();
+    }
+    c = n > 0 ? n : -1;
+  }
+  return c > 0 ? c : 0;
 }
 
 hipError_t launch_merge_kernel(const MergeParams& p, hipStream_t stream) {

@@ -53,6 +53,19 @@ def test_baseline_split_rule_matches_golden(lib):
     assert binding.num_kv_splits_baseline(-1, 256) == 0 and binding.num_kv_splits_baseline(100, 0) == 0
 
 
+def _expected_workspace(B, T, H, s, ws):
+    """Partials [B, T*H, s, 513] fp32; a single-launch call adds two 8-byte
+    words per (sequence, row block) after them (16-byte aligned)."""
+    if s == 1:
+        return ws == 0
+    partials = B * T * H * s * 513 * 4
+    if ws == partials:
+        return True
+    sync = ws - (partials + 15) // 16 * 16
+    row_blocks = -(-T * H // 32)                    # at most one group per 32 rows
+    return sync > 0 and sync % 16 == 0 and sync <= 16 * B * row_blocks
+
+
 @pytest.mark.parametrize("B,T,H,L,K,fp8", [
     (2, 1, 16, 300, 0, False), (128, 1, 16, 8192, 0, False), (64, 4, 32, 80000, 0, True),
     (32, 8, 128, 32768, 0, False), (64, 1, 128, 65536, 2048, False), (3, 2, 24, 5000, 300, False)])
@@ -60,10 +73,10 @@ def test_workspace_matches_split_count(lib, B, T, H, L, K, fp8):
     s = binding.num_kv_splits(B, T, H, L, K, fp8)
     assert 1 <= s <= binding.MAX_KV_SPLITS
     ws = binding.workspace_size(B, T, H, L, K, fp8, 0)
-    assert ws == (0 if s == 1 else B * T * H * s * 513 * 4)
+    assert _expected_workspace(B, T, H, s, ws), (s, ws)
     for forced in (1, 2, 7):
         ws = binding.workspace_size(B, T, H, L, K, fp8, forced)
-        assert ws == (0 if forced == 1 else B * T * H * forced * 513 * 4)
+        assert _expected_workspace(B, T, H, forced, ws), (forced, ws)
 
 
 def test_heuristic_fills_the_chip(lib):
