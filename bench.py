@@ -130,6 +130,121 @@ def load_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def _timed(fn, steps, warmup, stream):
+    """Median / p10 / p90 of per-call HIP-event times (us) of fn() on stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2), "mean": round(float(us.mean()), 2)}
+
+
+def mha_vs_mqa(args):
+    """A prefill batch (q_len = L for every sequence, causal) whose sequences
+    all fit in top-k, run both ways on the same cache, queries and
+    up-projections:
+      * dense MHA: one mla_dense_mha call (expansion of the latents by
+        [W_UK; W_UV] and the attention, both in the library);
+      * sparse MQA: the query absorbed by W_UK (torch bmm), one
+        mla_sparse_decode call over one single-query row per token whose
+        index list holds every position it sees, the latent output
+        projected by W_UV (torch bmm).
+    Prints one JSON line: both times, the speed-up, the dense call's MFMA
+    roofline, and the largest difference between the two outputs."""
+    import torch
+    from mla_paged_latent_03_amd import binding, workloads as wl
+
+    B, L, H, K = args.mha_batch, args.mha_len, args.mha_heads, 2048
+    if L > K:
+        raise SystemExit("--mha-len must be <= top-k (2048): the dense route serves sequences that fit in top-k")
+    binding.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    name = "prefill_b%d_h%d_len%d_top%d_bf16" % (B, H, L, K)
+    log("[bench] drawing %s" % name)
+    inp = wl.make_inputs(B, H, L, [L] * B, kv_dtype="bf16", out_dtype="bf16", seed=1101, device=dev, name=name)
+    q, w_uk, w_uv = wl.mha_inputs(inp, seed=1102, device=dev)
+    rows = B * L
+
+    out_mha = torch.empty((B, L, H, 128), device=dev, dtype=torch.bfloat16)
+    lse_mha = torch.empty((B, L, H), device=dev, dtype=torch.float32)
+    ws_mha = torch.empty((binding.dense_mha_workspace_size(B, H, L) + 1) // 2, device=dev, dtype=torch.bfloat16)
+
+    def mha():
+        binding.mla_dense_mha(q, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, w_uk, w_uv, L,
+                              inp.softmax_scale, out_mha, lse_mha, ws_mha, stream)
+
+    # MQA side: per-head batched products with contiguous operands.
+    q_h = q.reshape(rows, H, 128).transpose(0, 1).contiguous()            # [H, rows, 128]
+    w_uv_t = w_uv.transpose(1, 2).contiguous()                            # [H, 512, 128]
+    q_abs_h = torch.empty((H, rows, 512), device=dev, dtype=torch.bfloat16)
+    q_abs = torch.empty((rows, H, 512), device=dev, dtype=torch.bfloat16)
+    sp = wl.prefill_rows_as_sparse_decode(inp, q_abs.reshape(B, L, H, 512), K)
+    assert sp.q_nope.data_ptr() == q_abs.data_ptr()
+    lat = torch.empty((rows, 1, H, 512), device=dev, dtype=torch.bfloat16)
+    lse_mqa = torch.empty((rows, 1, H), device=dev, dtype=torch.float32)
+    S = binding.num_kv_splits(rows, 1, H, L, K, False)
+    need = binding.workspace_size(rows, 1, H, L, K, False, S)
+    ws_mqa = torch.empty(max(1, (need + 3) // 4), device=dev, dtype=torch.float32)
+    lat_h = torch.empty((H, rows, 512), device=dev, dtype=torch.bfloat16)
+    out_mqa_h = torch.empty((H, rows, 128), device=dev, dtype=torch.bfloat16)
+
+    def absorb():
+        torch.bmm(q_h, w_uk, out=q_abs_h)
+        q_abs.copy_(q_abs_h.transpose(0, 1))        # sp.q_nope is a view of q_abs
+
+    def attend():
+        binding.mla_sparse_decode(sp.q_nope, sp.q_pe, sp.kv_cache, sp.block_table, sp.seq_lens, sp.topk_indices,
+                                  L, sp.softmax_scale, lat, lse_mqa, ws_mqa, S, stream)
+
+    def project():
+        lat_h.copy_(lat.view(rows, H, 512).transpose(0, 1))
+        torch.bmm(lat_h, w_uv_t, out=out_mqa_h)
+
+    def mqa():
+        absorb()
+        attend()
+        project()
+
+    t_mha = _timed(mha, args.steps, args.warmup, stream)
+    t_mqa = _timed(mqa, args.steps, args.warmup, stream)
+    t_attend = _timed(attend, args.steps, args.warmup, stream)
+    mha()
+    mqa()
+    torch.cuda.synchronize()
+    diff = float((out_mha.float().reshape(rows, H, 128) - out_mqa_h.float().transpose(0, 1)).abs().max())
+    lse_diff = float((lse_mha.reshape(-1) - lse_mqa.reshape(-1)).abs().max())
+    pairs = H * B * L * (L + 1) // 2
+    flops_expand = 2 * B * L * H * 256 * 512
+    flops_attn = pairs * 2 * (192 + 128)
+    flops = flops_expand + flops_attn
+    ach = flops / (t_mha["median"] * 1e-6) / 1e12
+    res = {
+        "metric": "dense MHA vs sparse MQA on a prefill batch that fits in top-k: us per batch",
+        "value": t_mha["median"], "unit": "us/batch", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic (seeded N(0,1) latents and queries, "
+        "N(0,1/512) up-projections, shuffled pages)",
+        "config": {"workload": name, "batch": B, "heads": H, "q_len": L, "seq_len": L, "topk": K,
+                   "mqa_rows": rows, "mqa_kv_splits": S},
+        "mha_us": t_mha, "mqa_us": t_mqa, "mqa_attention_only_us": t_attend,
+        "speedup_mha_over_mqa": round(t_mqa["median"] / t_mha["median"], 3),
+        "roofline": {"bound": "mfma", "kernel": "mla_dense_mha (expand + attention)",
+                     "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(ach / MFMA_PEAK_TFLOPS["bf16"], 4), "flops": flops,
+                     "flops_expand": flops_expand, "flops_attention": flops_attn},
+        "max_abs_out_diff_mha_vs_mqa": round(diff, 5), "max_abs_lse_diff_mha_vs_mqa": round(lse_diff, 5),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +258,12 @@ def main():
                     help="request the single-launch form (MLA_SINGLE_LAUNCH=1): split units merge in-kernel")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mha-vs-mqa", action="store_true",
+                    help="instead: a prefill batch whose sequences all fit in top-k, through the dense "
+                         "un-absorbed MHA call and through the sparse absorbed MQA call on the same inputs")
+    ap.add_argument("--mha-batch", type=int, default=4)
+    ap.add_argument("--mha-len", type=int, default=2048, help="sequence length = query tokens (prefill)")
+    ap.add_argument("--mha-heads", type=int, default=128)
     ap.add_argument("--copy-calibration-gib", type=int, default=0,
                     help="first copy a buffer of this many GiB three times, so that a counter run over the "
                          "benchmark also reads the counters for a plain copy of known size")
@@ -153,6 +274,9 @@ def main():
               "(its sequence-sharded multi-GPU form is not implemented). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.mha_vs_mqa:
+        mha_vs_mqa(args)
+        return
     if args.single_launch:
         os.environ["MLA_SINGLE_LAUNCH"] = "1"
     else:

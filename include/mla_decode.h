@@ -127,6 +127,7 @@ enum { MLA_OUT_BF16 = 0, MLA_OUT_F32 = 1 };
 #define MLA_BLOCK_SIZE 64
 #define MLA_MAX_Q_LEN 8
 #define MLA_MAX_KV_SPLITS 256
+#define MLA_MHA_MAX_Q_LEN 65536   /* mla_dense_mha only: query tokens per sequence */
 
 /* Static text for a status code (never NULL). */
 const char* mla_status_string(mla_status_t status);
@@ -249,6 +250,40 @@ mla_status_t mla_decode_fp8_noalloc(const void* q_nope, const void* q_pe, const 
                                     int max_blocks_per_seq, int max_seq_len, float softmax_scale,
                                     float q_scale, float kv_scale, void* out, int out_dtype, float* lse,
                                     int num_kv_splits, void* stream);
+
+/*
+ * Dense un-absorbed multi-head attention over the paged latent cache: the
+ * route the pages take for sparse-MLA batches whose sequences all fit in
+ * top-k (then every position is in the top-k list, so the attention is
+ * dense), "subject to a q_len threshold" (vLLM PR #47327 digest,
+ * "Summary" and "Implementation" item 2).  Each head h expands the cached
+ * latents with its own up-projections (DeepSeek-R1 dims: 128 no-rope + 64
+ * rope for keys, 128 for values; vLLM PR #41778 digest, "Risks and impact"
+ * item 4):
+ *     k[h,j] = [ W_UK[h] c_j ; r_j ]  (192)     v[h,j] = W_UV[h] c_j  (128)
+ *     out[b,t,h,:] = sum_j softmax_j(softmax_scale * <q[b,t,h], k[h,j]>) v[h,j]
+ *     lse[b,t,h]   = ln sum_j exp(softmax_scale * <q[b,t,h], k[h,j]>)
+ * over positions j = 0 .. seq_lens[b] - q_len + t (causal, as in the
+ * decode calls; with q_len = seq_lens[b] this is a whole prefill).  It pays
+ * off over the absorbed form when many query tokens share a sequence's
+ * expansion, and costs far more than it at decode sizes.
+ *   q_nope   [B, T, H, 128] bf16   un-absorbed no-rope query
+ *   q_pe     [B, T, H, 64]  bf16   rope query
+ *   kv_cache, block_table, seq_lens, block_size, max_seq_len as mla_decode
+ *   w_uk, w_uv [H, 128, 512] bf16  W_UK[h][d][k], W_UV[h][d][k]
+ *   out      [B, T, H, 128] in out_dtype; lse [B, T, H] fp32 or NULL
+ *   workspace >= mla_dense_mha_workspace_size(B, H, max_seq_len) bytes
+ *             (the expanded K and V, bf16); contents on entry ignored
+ * q_len is 1 .. MLA_MHA_MAX_Q_LEN.  Rows that see no token get 0 and -inf.
+ * Two kernels on `stream` (expansion, then attention); no allocation.
+ */
+size_t mla_dense_mha_workspace_size(int batch, int num_heads, int max_seq_len);
+mla_status_t mla_dense_mha(const void* q_nope, const void* q_pe, const void* kv_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, const void* w_uk,
+                           const void* w_uv, int batch, int q_len, int num_heads, int num_blocks,
+                           int block_size, int max_blocks_per_seq, int max_seq_len,
+                           float softmax_scale, void* out, int out_dtype, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Top-k sparse bf16 decode.  topk_indices [B, T, K] int32 lists, per query

@@ -23,7 +23,9 @@ MLA_OUT_BF16, MLA_OUT_F32 = 0, 1
 MAX_KV_SPLITS = 256
 EXPORTS = ("mla_status_string", "mla_num_kv_splits", "mla_launch_waves", "mla_workspace_size",
            "mla_num_kv_splits_baseline", "mla_decode", "mla_decode_fp8", "mla_decode_fp8_noalloc",
-           "mla_sparse_decode", "mla_sparse_decode_fp8", "mla_merge_partials")
+           "mla_sparse_decode", "mla_sparse_decode_fp8", "mla_merge_partials", "mla_dense_mha",
+           "mla_dense_mha_workspace_size")
+MHA_MAX_Q_LEN = 65536
 
 _lib = None
 
@@ -66,6 +68,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_sparse_decode_fp8.restype = c_int
     lib.mla_sparse_decode_fp8.argtypes = ([vp, vp, vp, vp, vp, vp, c_int] + [c_int] * 7 + [c_float, c_float, c_float]
                                           + common_tail[1:])
+    lib.mla_dense_mha_workspace_size.restype = c_size
+    lib.mla_dense_mha_workspace_size.argtypes = [c_int] * 3
+    lib.mla_dense_mha.restype = c_int
+    lib.mla_dense_mha.argtypes = [vp] * 7 + [c_int] * 7 + [c_float, vp, c_int, vp, vp, c_size, vp]
     lib.mla_merge_partials.restype = c_int
     lib.mla_merge_partials.argtypes = [vp, ctypes.c_int64, c_int, vp, c_int, vp, vp]
     _lib = lib
@@ -191,6 +197,29 @@ def mla_sparse_decode_fp8(q_nope, q_pe, kv_cache, block_table, seq_lens, topk_in
                                       _ptr(out), _out_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                       int(num_kv_splits), _stream(stream))
     _check(st, "mla_sparse_decode_fp8")
+
+
+def dense_mha_workspace_size(batch, num_heads, max_seq_len) -> int:
+    return load().mla_dense_mha_workspace_size(batch, num_heads, max_seq_len)
+
+
+def mla_dense_mha(q_nope, q_pe, kv_cache, block_table, seq_lens, w_uk, w_uv, max_seq_len, softmax_scale, out,
+                  lse=None, workspace=None, stream=None):
+    """Dense un-absorbed MHA (mla_dense_mha).  q_nope [B,T,H,128], q_pe [B,T,H,64],
+    w_uk / w_uv [H,128,512] bf16; out [B,T,H,128].  Allocates the workspace with
+    torch when not given; returns it."""
+    B, T, H, _ = q_nope.shape
+    NB, P, _ = kv_cache.shape
+    if workspace is None:
+        need = dense_mha_workspace_size(B, H, int(max_seq_len))
+        workspace = torch.empty(max(1, (need + 1) // 2), device=q_nope.device, dtype=torch.bfloat16)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().mla_dense_mha(_ptr(q_nope), _ptr(q_pe), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+                              _ptr(w_uk), _ptr(w_uv), B, T, H, NB, P, block_table.shape[1], int(max_seq_len),
+                              float(softmax_scale), _ptr(out), _out_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                              _stream(stream))
+    _check(st, "mla_dense_mha")
+    return workspace
 
 
 def mla_merge_partials(workspace, rows, num_kv_splits, out, lse=None, stream=None):

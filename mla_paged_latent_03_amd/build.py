@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = [os.path.join(CSRC, "mla_decode_kernels.hip"), os.path.join(CSRC, "mla_decode_api.cpp")]
+SOURCES = [os.path.join(CSRC, "mla_decode_kernels.hip"), os.path.join(CSRC, "mla_decode_api.cpp"),
+           os.path.join(CSRC, "mla_mha_kernels.hip"), os.path.join(CSRC, "mla_mha_api.cpp")]
 # Benchmark-only: the streaming-read reference kernel (not part of the decode ABI).
 STREAM_LIB = os.path.join(HERE, "libmla_stream_ref.so")
 STREAM_SRC = os.path.join(CSRC, "stream_ref.hip")

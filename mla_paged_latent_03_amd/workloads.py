@@ -231,3 +231,41 @@ def as_numpy_bits(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
     return t.numpy()
+
+
+def mha_inputs(inp: DecodeInputs, seed: int, device=None):
+    """Inputs of the un-absorbed route for the same cache: an un-absorbed
+    no-rope query [B, T, H, 128] and per-head up-projections W_UK, W_UV
+    [H, 128, 512], bf16.  Queries ~ N(0, 1); projection entries
+    ~ N(0, 1/512), so that the expanded keys and values are about N(0, 1)
+    like the latents.  Drawn from a CPU generator."""
+    device = inp.q_nope.device if device is None else device
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((inp.B, inp.T, inp.H, 128), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    w = (torch.randn((2, inp.H, 128, D_LATENT), generator=g, dtype=torch.float32) / math.sqrt(D_LATENT))
+    w = w.to(torch.bfloat16)
+    return q.to(device), w[0].contiguous().to(device), w[1].contiguous().to(device)
+
+
+def prefill_rows_as_sparse_decode(inp: DecodeInputs, q_abs: torch.Tensor, topk: int) -> DecodeInputs:
+    """The same causal attention as a q_len-T call over ``inp``'s cache, laid
+    out for the sparse decode: one single-query row per (sequence, query
+    token), its index list holding every position that token sees
+    (0 .. L - T + t, then -1 up to ``topk``).  ``q_abs`` [B, T, H, 512] is
+    the absorbed query; the rope part is ``inp.q_pe``.  Needs
+    L - T + t + 1 <= topk for every row."""
+    B, T, H = inp.B, inp.T, inp.H
+    dev = inp.q_nope.device
+    lens = inp.seq_lens.to(torch.int64)
+    n_vis = (lens[:, None] - T + torch.arange(T, device=dev)[None, :] + 1).clamp(min=0).reshape(-1)
+    if int(n_vis.max().item()) > topk:
+        raise ValueError("a row sees more positions than topk")
+    pos = torch.arange(topk, device=dev, dtype=torch.int32)[None, :]
+    idx = torch.where(pos < n_vis[:, None], pos, torch.full_like(pos, -1))
+    return DecodeInputs(q_nope=q_abs.reshape(B * T, 1, H, D_LATENT).contiguous(),
+                        q_pe=inp.q_pe.reshape(B * T, 1, H, D_ROPE).contiguous(), kv_cache=inp.kv_cache,
+                        block_table=inp.block_table.repeat_interleave(T, dim=0).contiguous(),
+                        seq_lens=inp.seq_lens.repeat_interleave(T).contiguous(),
+                        topk_indices=idx.reshape(B * T, 1, topk).contiguous(), kv_dtype=inp.kv_dtype,
+                        out_dtype=inp.out_dtype, softmax_scale=inp.softmax_scale, name=inp.name + "_as_rows",
+                        seed=inp.seed, max_len=inp.max_len)

@@ -257,3 +257,48 @@ def test_noalloc_refuses_partials_beyond_its_static_buffer(lib):
     st = lib.mla_decode_fp8_noalloc(fake, fake, fake, fake, fake, B, 9, H, 100, 64, 1250, L, 0.07, 1.0, 1.0, fake,
                                     0, fake, 2, None)
     assert st == binding.MLA_ERR_INVALID_ARGUMENT
+
+
+# ------------------------------------------------------------------ dense un-absorbed MHA route
+
+def test_dense_mha_workspace_formula(lib):
+    """K_nope [B, H, Lpad, 128] and V^T [B, H, 128, Lpad] bf16, Lpad = max_seq_len
+    rounded up to 32."""
+    for B, H, L in ((2, 16, 300), (1, 1, 1), (3, 128, 8192), (4, 8, 0), (1, 2, 32)):
+        lpad = (L + 31) // 32 * 32
+        assert binding.dense_mha_workspace_size(B, H, L) == 2 * B * H * lpad * 128 * 2
+    assert binding.dense_mha_workspace_size(-1, 16, 100) == 0
+    assert binding.dense_mha_workspace_size(1, 0, 100) == 0
+    assert binding.dense_mha_workspace_size(1, 16, -5) == 0
+
+
+def _call_mha(lib, **kw):
+    a = dict(q=FAKE, qpe=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, wk=FAKE, wv=FAKE, B=2, T=4, H=16, NB=10, P=64, MB=5,
+             msl=300, scale=0.07, out=FAKE, odt=0, lse=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.mla_dense_mha(a["q"], a["qpe"], a["kv"], a["bt"], a["sl"], a["wk"], a["wv"], a["B"], a["T"], a["H"],
+                             a["NB"], a["P"], a["MB"], a["msl"], a["scale"], a["out"], a["odt"], a["lse"], a["ws"],
+                             a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(T=binding.MHA_MAX_Q_LEN + 1), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(P=32), binding.MLA_ERR_UNSUPPORTED),
+    (dict(wk=None), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(wv=FAKE + 2), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(odt=3), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(MB=0), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(wsb=2 * 2 * 16 * 320 * 128 * 2 - 1), binding.MLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=None), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(ws=FAKE + 8), binding.MLA_ERR_INVALID_ARGUMENT),
+])
+def test_dense_mha_argument_errors(lib, kw, status):
+    assert _call_mha(lib, **kw) == status
+
+
+def test_dense_mha_empty_batch_is_a_no_op(lib):
+    assert _call_mha(lib, B=0, q=None, out=None, ws=None, wsb=0) == binding.MLA_OK

@@ -299,3 +299,93 @@ def test_baseline_split_rule_golden_table(oracle_lib):
         cases = json.load(f)["cases"]
     for c in cases:
         assert oracle.num_kv_splits_baseline(c["max_seq_len"], c["sm_count"]) == c["splits"], c
+
+
+def test_paged_unabsorbed_mha_equals_projected_absorbed_oracle(oracle_lib):
+    """The un-absorbed paged oracle (mha_bruteforce.mha_paged: its own paging,
+    causal list and per-head expansion) against the C oracle's absorbed
+    decode of q_abs = W_UK^T q_nope, projected by W_UV: the same attention,
+    so equal to rounding (W_UK absorbed exactly in fp64), MTP rows that see
+    nothing included."""
+    import oracle.mha_bruteforce as mb
+    rng = np.random.default_rng(31)
+    B, T, H, P = 3, 3, 4, 16
+    lens = [1, 20, 45]
+    pages = [(L + P - 1) // P for L in lens]
+    NB = sum(pages) + 2
+    perm = rng.permutation(NB)
+    bt = np.full((B, max(pages)), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    kv = rng.standard_normal((NB, P, 576))
+    q_nope = rng.standard_normal((B, T, H, 128))
+    q_pe = rng.standard_normal((B, T, H, 64))
+    w_uk = rng.standard_normal((H, 128, 512)) / np.sqrt(512)
+    w_uv = rng.standard_normal((H, 128, 512)) / np.sqrt(512)
+    scale = 1 / np.sqrt(192)
+    o_mha, l_mha = mb.mha_paged(q_nope, q_pe, kv, bt, np.array(lens), w_uk, w_uv, scale)
+    q_abs = np.stack([[mb.absorb_query(q_nope[b, t], w_uk) for t in range(T)] for b in range(B)])
+    o_lat, l_lat = oracle.decode(q_abs, q_pe, kv, bt, np.array(lens, dtype=np.int32), softmax_scale=scale)
+    o_proj = np.stack([mb.project_output(o_lat.reshape(B, T, H, 512)[b, t], w_uv) for b in range(B)
+                       for t in range(T)]).reshape(-1, 128)
+    fin = np.isfinite(l_lat)
+    assert np.array_equal(np.isneginf(l_mha), np.isneginf(l_lat)) and (~fin).sum() == H * 2   # b=0: t=0,1 empty
+    assert np.allclose(l_mha[fin], l_lat[fin], atol=1e-10, rtol=0)
+    assert np.allclose(o_mha, o_proj, atol=1e-10, rtol=0)
+
+
+def test_round_bf16_ties_and_one_step_rounding():
+    """bf16 keeps 8 significant bits: the quantum at 1 is 2^-7; ties go to
+    the even neighbour; the rounding is taken once from the float64 value
+    (1 + 2^-8 + 2^-30 is above the tie, though float32 would first round it
+    onto the tie and then down to 1)."""
+    r = mha.round_bf16
+    cases = [(1.0 + 2.0 ** -8, 1.0), (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6), (1.0 + 2.0 ** -8 + 2.0 ** -30,
+             1.0 + 2.0 ** -7), (-(1.0 + 2.0 ** -8 + 2.0 ** -40), -(1.0 + 2.0 ** -7)), (0.0, 0.0),
+             (3.0, 3.0), (255.5, 256.0), (257.0, 256.0), (259.0, 260.0), (2.0 ** -130 * 1.25, 2.0 ** -130 * 1.25),
+             (2.0 ** -133 * 1.5, 2.0 ** -132), (2.0 ** -134, 0.0)]
+    for x, want in cases:
+        assert r(np.float64(x)) == want, (x, r(np.float64(x)), want)
+
+
+def test_round_bf16_agrees_with_torch_on_float32_inputs():
+    """On float32 inputs one-step rounding is torch's float32 -> bfloat16 cast
+    (round to nearest even), normals and subnormals alike."""
+    g = torch.Generator().manual_seed(41)
+    x = torch.randn(20000, generator=g) * torch.exp2(torch.randint(-140, 60, (20000,), generator=g).float())
+    x = torch.cat([x, torch.tensor([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.0 ** -127, 2.0 ** -149])])
+    want = x.to(torch.bfloat16).double().numpy()
+    got = mha.round_bf16(x.double().numpy())
+    assert np.array_equal(got, want)
+
+
+def test_bf16_expanded_mha_rounds_the_expanded_keys_and_values():
+    """With selection matrices for W_UK and W_UV (each output row picks one
+    latent feature), the up-projection copies latents, so rounding the
+    expanded keys and values equals rounding the cache's latent part first
+    and expanding exactly; with bf16-exact latents the two modes agree."""
+    import oracle.mha_bruteforce as mb
+    rng = np.random.default_rng(43)
+    B, T, H, P = 2, 2, 3, 16
+    lens = [20, 33]
+    bt = np.array([[0, 1, -1], [2, 3, 4]], dtype=np.int32)
+    kv = rng.standard_normal((5, P, 576))
+    q_nope = rng.standard_normal((B, T, H, 128))
+    q_pe = rng.standard_normal((B, T, H, 64))
+    w_uk = np.zeros((H, 128, 512))
+    w_uv = np.zeros((H, 128, 512))
+    for h in range(H):
+        w_uk[h, np.arange(128), rng.permutation(512)[:128]] = 1.0
+        w_uv[h, np.arange(128), rng.permutation(512)[:128]] = 1.0
+    scale = 1 / np.sqrt(192)
+    o_b, l_b = mb.mha_paged(q_nope, q_pe, kv, bt, np.array(lens), w_uk, w_uv, scale, expanded="bf16")
+    kv_r = kv.copy()
+    kv_r[..., :512] = mb.round_bf16(kv[..., :512])
+    o_f, l_f = mb.mha_paged(q_nope, q_pe, kv_r, bt, np.array(lens), w_uk, w_uv, scale, expanded="f64")
+    assert np.array_equal(o_b, o_f) and np.array_equal(l_b, l_f)
+    o_u, _ = mb.mha_paged(q_nope, q_pe, kv, bt, np.array(lens), w_uk, w_uv, scale, expanded="f64")
+    assert np.abs(o_u - o_b).max() > 1e-6          # the rounding is not a no-op
+    o_e, l_e = mb.mha_paged(q_nope, q_pe, kv_r, bt, np.array(lens), w_uk, w_uv, scale, expanded="bf16")
+    assert np.array_equal(o_e, o_f) and np.array_equal(l_e, l_f)
