@@ -171,14 +171,6 @@ size_t mla_workspace_size(int batch, int q_len, int num_heads, int max_seq_len, 
                           int kv_fp8, int num_kv_splits);
 
 /*
- * The Triton MLA decode's split rule, kept for comparison:
- * min(next_pow2(max(1, max_seq_len / 512)), 2 * sm_count)  (vLLM PR #46819
- * digest, "Key code excerpt").  Not used by the decode calls.  Returns 0 on
- * invalid arguments.
- */
-int mla_num_kv_splits_baseline(int max_seq_len, int sm_count);
-
-/*
  * Dense bf16 decode.
  *   q_nope      [B, T, H, 512] bf16   absorbed no-rope query
  *   q_pe        [B, T, H, 64]  bf16   rope query

@@ -22,7 +22,7 @@ STATIC_SCRATCH_BYTES = 64 << 20
 MLA_OUT_BF16, MLA_OUT_F32 = 0, 1
 MAX_KV_SPLITS = 256
 EXPORTS = ("mla_status_string", "mla_num_kv_splits", "mla_launch_waves", "mla_workspace_size",
-           "mla_num_kv_splits_baseline", "mla_decode", "mla_decode_fp8", "mla_decode_fp8_noalloc",
+           "mla_decode", "mla_decode_fp8", "mla_decode_fp8_noalloc",
            "mla_sparse_decode", "mla_sparse_decode_fp8", "mla_merge_partials", "mla_dense_mha",
            "mla_dense_mha_workspace_size")
 MHA_MAX_Q_LEN = 65536
@@ -53,8 +53,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_launch_waves.argtypes = [c_int] * 6
     lib.mla_workspace_size.restype = c_size
     lib.mla_workspace_size.argtypes = [c_int] * 7
-    lib.mla_num_kv_splits_baseline.restype = c_int
-    lib.mla_num_kv_splits_baseline.argtypes = [c_int, c_int]
     common_tail = [c_float, vp, c_int, vp, vp, c_size, c_int, vp]
     lib.mla_decode.restype = c_int
     lib.mla_decode.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 7 + common_tail
@@ -96,8 +94,6 @@ def workspace_size(batch, q_len, num_heads, max_seq_len, topk=0, kv_fp8=False, n
                                      num_kv_splits)
 
 
-def num_kv_splits_baseline(max_seq_len, sm_count) -> int:
-    return load().mla_num_kv_splits_baseline(max_seq_len, sm_count)
 
 
 def _ptr(t: Optional[torch.Tensor]):

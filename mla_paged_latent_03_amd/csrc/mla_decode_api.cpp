@@ -373,17 +373,6 @@ size_t mla_workspace_size(int batch, int q_len, int num_heads, int max_seq_len, 
   return pl.ws_bytes;
 }
 
-int mla_num_kv_splits_baseline(int max_seq_len, int sm_count) {
-  if (max_seq_len < 0 || sm_count < 1) return 0;
-  const int min_work_per_split = 512, occupancy_multiplier = 2;
-  int ideal = max_seq_len / min_work_per_split;
-  if (ideal < 1) ideal = 1;
-  int pow2 = 1;
-  while (pow2 < ideal) pow2 <<= 1;
-  const int cap = sm_count * occupancy_multiplier;
-  return pow2 < cap ? pow2 : cap;
-}
-
 mla_status_t mla_decode(const void* q_nope, const void* q_pe, const void* kv_cache, const int32_t* block_table,
                         const int32_t* seq_lens, int batch, int q_len, int num_heads, int num_blocks,
                         int block_size, int max_blocks_per_seq, int max_seq_len, float softmax_scale, void* out,

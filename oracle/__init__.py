@@ -14,5 +14,4 @@ from .oracle import (  # noqa: F401
     decode,
     e4m3fn_to_float64,
     bf16_bits_to_float64,
-    num_kv_splits_baseline,
 )

@@ -134,15 +134,3 @@ def e4m3fn_to_float64(byte: int) -> float:
 
 def bf16_bits_to_float64(bits: int) -> float:
     return _load().orc_bf16_to_double(int(bits))
-
-
-def num_kv_splits_baseline(max_seq_len: int, sm_count: int) -> int:
-    """The split-count rule of the Triton MLA decode (vLLM PR #46819 digest,
-    "Key code excerpt"): one split per 512 tokens rounded up to a power of
-    two, capped at two splits per compute unit."""
-    min_work_per_split, occupancy_multiplier = 512, 2
-    ideal = max(1, max_seq_len // min_work_per_split)
-    pow2 = 1
-    while pow2 < ideal:
-        pow2 *= 2
-    return min(pow2, sm_count * occupancy_multiplier)

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mla_decode", "mla_decode_fp8", "mla_sparse_decode", "mla_workspace_size", "mla_num_kv_splits",
-              "mla_status_string", "mla_num_kv_splits_baseline"):
+              "mla_status_string"):
         assert n in names, n
 
 
@@ -44,13 +44,6 @@ def test_status_strings(lib):
     assert binding.status_string(0) == "ok"
     assert binding.status_string(3) == "workspace too small"
     assert binding.status_string(99) == "unknown status"
-
-
-def test_baseline_split_rule_matches_golden(lib):
-    with open(os.path.join(ROOT, "tests", "golden", "kv_splits_baseline.json")) as f:
-        for c in json.load(f)["cases"]:
-            assert binding.num_kv_splits_baseline(c["max_seq_len"], c["sm_count"]) == c["splits"], c
-    assert binding.num_kv_splits_baseline(-1, 256) == 0 and binding.num_kv_splits_baseline(100, 0) == 0
 
 
 def _expected_workspace(B, T, H, s, ws):
@@ -240,6 +233,28 @@ def test_asm_hazard_scan_flags_m0_and_sgpr_hazards():
     nt_sparse = _asm("s_add_i32 m0, s37, 0x400", ";;#ASMSTART", "global_load_lds_dwordx4 v[2:3], off nt",
                      ";;#ASMEND")
     assert len(hz.scan(nt_sparse)) == 1
+
+
+def test_asm_hazard_scan_follows_branches_into_a_block():
+    """A block entered by a branch: the fall-through path into it has its
+    wait states, the branch path does not (the hazard class of the fault
+    fixed by the s_nop in the descriptor set-up).  Also a loop back-edge,
+    and an unconditional branch that ends the fall-through path."""
+    from mla_paged_latent_03_amd import asm_hazards as hz
+    branch_entered = _asm("v_readfirstlane_b32 s9, v0", "s_cbranch_scc1 .LBB0_2", "s_nop 4", "s_mov_b32 m0, s1",
+                          ".LBB0_2:", ";;#ASMSTART", "s_nop 0", _DMA, ";;#ASMEND")
+    found = hz.scan(branch_entered)
+    assert len(found) == 1 and "v_readfirstlane_b32 s9" in found[0]
+    both_settled = _asm("v_readfirstlane_b32 s9, v0", "s_nop 4", "s_cbranch_scc1 .LBB0_2", "s_nop 4",
+                        "s_mov_b32 m0, s1", ".LBB0_2:", ";;#ASMSTART", "s_nop 0", _DMA, ";;#ASMEND")
+    assert hz.scan(both_settled) == []
+    back_edge = _asm("s_mov_b32 m0, s1", "s_nop 4", ".LBB0_1:", ";;#ASMSTART", "s_nop 0", _DMA, ";;#ASMEND",
+                     "s_add_u32 s20, s20, 1", "v_readlane_b32 s12, v5, 0", "s_cbranch_scc1 .LBB0_1")
+    found = hz.scan(back_edge)
+    assert len(found) == 1 and "v_readlane_b32 s12" in found[0]
+    no_fallthrough = _asm("v_readfirstlane_b32 s9, v0", "s_branch .LBB0_3", ".LBB0_2:", ";;#ASMSTART", "s_nop 0",
+                          _DMA, ";;#ASMEND", ".LBB0_3:", "s_endpgm")
+    assert hz.scan(no_fallthrough) == []
 
 
 def test_noalloc_refuses_partials_beyond_its_static_buffer(lib):

@@ -294,13 +294,6 @@ def test_tiny_workload_against_numpy_dense_softmax(oracle_lib):
         np.testing.assert_allclose(l[b], (m[:, 0] + np.log(w.sum(axis=1))), rtol=1e-13)
 
 
-def test_baseline_split_rule_golden_table(oracle_lib):
-    with open(os.path.join(GOLDEN, "kv_splits_baseline.json")) as f:
-        cases = json.load(f)["cases"]
-    for c in cases:
-        assert oracle.num_kv_splits_baseline(c["max_seq_len"], c["sm_count"]) == c["splits"], c
-
-
 def test_paged_unabsorbed_mha_equals_projected_absorbed_oracle(oracle_lib):
     """The un-absorbed paged oracle (mha_bruteforce.mha_paged: its own paging,
     causal list and per-head expansion) against the C oracle's absorbed
