@@ -66,8 +66,11 @@
  * Conventions shared by every entry point:
  *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
  *    row-major, on the current HIP device.  The library allocates nothing
- *    and keeps no state between calls; its launch plan assumes the 256
- *    compute units of an MI355X.
+ *    and keeps no state between calls beyond two caches: the compute-unit
+ *    count of each device and the resident workgroups per compute unit of
+ *    each kernel variant, both asked of the runtime once (256 and the LDS
+ *    model are assumed where no device can be asked).  Plans follow the
+ *    device's count, so a partitioned MI355X gets a plan for its share.
  *  - Calls enqueue on `stream` (a hipStream_t; NULL = the null stream) and
  *    return without synchronizing; they are safe to capture in a HIP graph.
  *  - Scales are read on every call and never cached (the pages record a
@@ -129,12 +132,19 @@ enum { MLA_OUT_BF16 = 0, MLA_OUT_F32 = 1 };
 #define MLA_MAX_KV_SPLITS 256
 #define MLA_MHA_MAX_Q_LEN 65536   /* mla_dense_mha only: query tokens per sequence */
 
-/* Static text for a status code (never NULL). */
+/* Static text for a status code (never NULL).  A convenience of this library,
+ * not an operation of the pages. */
 const char* mla_status_string(mla_status_t status);
 
 /*
  * Split count (partial slots per sequence) the library picks for a call when
- * num_kv_splits = 0.  Work units are (sequence, row block, split).  Each
+ * num_kv_splits = 0.  The pages' Triton decode derives its split count from
+ * max_seq_len and the SM count, in one function shared by the workspace
+ * reservation and the kernel launch so that the two cannot drift (vLLM PR
+ * #46819 digest, "Implementation" item 1 and "Key code excerpt"); here the
+ * same function serves mla_workspace_size and the decode calls, and it is
+ * costed for the device's compute units instead of a fixed work-per-split
+ * rule.  Work units are (sequence, row block, split).  Each
  * candidate row-block width and split count is costed, for sequences of
  * max_seq_len, as the bytes it moves (the KV once per row block, plus the
  * fp32 partials written and read back when split) divided by how fully its
@@ -146,8 +156,10 @@ const char* mla_status_string(mla_status_t status);
  * one round of workgroup slots but not two (at most 64 sequences), gets 2:
  * its sequences are cut into pieces for two rounds, dispatched longest piece
  * first.  Passing the returned count explicitly gives the same launch.  Deterministic in its arguments; topk = 0 means a
- * dense call, otherwise a sparse call with that K.  Returns 0 on invalid
- * arguments.
+ * dense call, otherwise a sparse call with that K.  kv_fp8 (nonzero for the
+ * fp8 calls) is an argument the pages' rule does not have: the fp8 kernels
+ * hold the same tile in half the LDS, and their residency, which the
+ * costing uses, differs.  Returns 0 on invalid arguments.
  */
 int mla_num_kv_splits(int batch, int q_len, int num_heads, int max_seq_len, int topk,
                       int kv_fp8);
@@ -156,13 +168,19 @@ int mla_num_kv_splits(int batch, int q_len, int num_heads, int max_seq_len, int 
  * Waves per workgroup (1, 2 or 4; each wave owns 32 query rows) that a call
  * with these arguments launches.  Follows from the shape alone, whatever
  * num_kv_splits is; lets tests and tuning tell which kernel variant a shape
- * runs.  Returns 0 on invalid arguments.
+ * runs.  A query of this library's plan, not an operation of the pages.
+ * Returns 0 on invalid arguments.
  */
 int mla_launch_waves(int batch, int q_len, int num_heads, int max_seq_len, int topk, int kv_fp8);
 
 /*
  * Workspace bytes a call needs: batch * q_len * num_heads * splits * 513 * 4,
- * or 0 when the call runs with one split; with the single launch (below)
+ * the fp32 partials of kv_lora_rank + 1 floats per (row, split) that the
+ * pages' Triton decode reserves ahead of time as [B, H, splits, 513]
+ * (vLLM PR #46819 digest, "Implementation" item 2 and "Key code excerpt";
+ * tokenspeed sizes its preallocated workspace with the same 513-float rows,
+ * vLLM PR #41778 digest, "Implementation" item 1), or 0 when the call runs
+ * with one split; with the single launch (below)
  * rounded up to 16 and followed by 16 bytes per (sequence, row block).  num_kv_splits = 0 means the
  * heuristic choice above.  Returns 0 for invalid arguments as well; pass the
  * same arguments to the decode call.
@@ -247,8 +265,8 @@ mla_status_t mla_decode_fp8_noalloc(const void* q_nope, const void* q_pe, const 
  * Dense un-absorbed multi-head attention over the paged latent cache: the
  * route the pages take for sparse-MLA batches whose sequences all fit in
  * top-k (then every position is in the top-k list, so the attention is
- * dense), "subject to a q_len threshold" (vLLM PR #47327 digest,
- * "Summary" and "Implementation" item 2).  Each head h expands the cached
+ * dense), when the query count passes a threshold (vLLM PR #47327
+ * digest, "Summary" and "Implementation" item 2).  Each head h expands the cached
  * latents with its own up-projections (DeepSeek-R1 dims: 128 no-rope + 64
  * rope for keys, 128 for values; vLLM PR #41778 digest, "Risks and impact"
  * item 4):
@@ -265,7 +283,11 @@ mla_status_t mla_decode_fp8_noalloc(const void* q_nope, const void* q_pe, const 
  *   w_uk, w_uv [H, 128, 512] bf16  W_UK[h][d][k], W_UV[h][d][k]
  *   out      [B, T, H, 128] in out_dtype; lse [B, T, H] fp32 or NULL
  *   workspace >= mla_dense_mha_workspace_size(B, H, max_seq_len) bytes
- *             (the expanded K and V, bf16); contents on entry ignored
+ *             (the expanded K and V, bf16, each sequence padded to a multiple
+ *             of 128 tokens); contents on entry ignored
+ * The expanded keys and values are rounded to bf16 (the model's activation
+ * type; the pages leave it open), products accumulate in fp32, and the
+ * softmax weights enter the value product as bf16.
  * q_len is 1 .. MLA_MHA_MAX_Q_LEN.  Rows that see no token get 0 and -inf.
  * Two kernels on `stream` (expansion, then attention); no allocation.
  */

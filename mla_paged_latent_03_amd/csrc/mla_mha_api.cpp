@@ -15,7 +15,17 @@ bool mha_dims_ok(int B, int T, int H, int max_seq_len) {
          max_seq_len <= (1 << 24);
 }
 
-int64_t padded_len(int max_seq_len) { return ((int64_t)max_seq_len + 31) / 32 * 32; }
+int64_t padded_len(int max_seq_len) {
+  return ((int64_t)max_seq_len + mla::kMhaTokPad - 1) / mla::kMhaTokPad * mla::kMhaTokPad;
+}
+
+// Workgroups of each launch (one per 128 tokens or 128 queries of every
+// (sequence, head)) must fit a 32-bit grid.
+bool grid_ok(int B, int T, int H, int max_seq_len) {
+  const int64_t pairs = (int64_t)B * H;
+  const int64_t lim = (int64_t)1 << 30;
+  return pairs * (padded_len(max_seq_len) / mla::kMhaTokPad) <= lim && pairs * ((T + 127) / 128) <= lim;
+}
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
@@ -35,6 +45,7 @@ mla_status_t mla_dense_mha(const void* q_nope, const void* q_pe, const void* kv_
                            size_t workspace_bytes, void* stream) {
   if (block_size != MLA_BLOCK_SIZE) return MLA_ERR_UNSUPPORTED;
   if (!mha_dims_ok(batch, q_len, num_heads, max_seq_len)) return MLA_ERR_INVALID_ARGUMENT;
+  if (!grid_ok(batch, q_len, num_heads, max_seq_len)) return MLA_ERR_UNSUPPORTED;
   if (num_blocks < 0 || max_blocks_per_seq < 1 || (int64_t)num_blocks * MLA_BLOCK_SIZE > INT32_MAX)
     return MLA_ERR_INVALID_ARGUMENT;
   if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_INVALID_ARGUMENT;

@@ -13,16 +13,22 @@
 // over the tokens query t sees (causal: positions 0 .. L_b - T + t).
 //
 // Two kernels:
-//  * mha_expand_kernel: per (sequence, head, 32 tokens) a GEMM of the
+//  * mha_expand_kernel: per (sequence, head, 128 tokens) the GEMM of the
 //    gathered latents with [W_UK[h]; W_UV[h]] (256 x 512) on bf16 MFMA,
-//    writing K_nope as [token][128] and V transposed as [128][token] into
-//    the workspace, so that the attention reads both as contiguous rows;
-//  * mha_attn_kernel: per (sequence, head, 32 queries) a flash-attention
-//    loop over 32-key tiles: S^T = K Q^T (keys on the MFMA A side, the
-//    192-wide query in registers on the B side), online softmax in the log2
-//    domain with bf16 P, O^T += V^T P^T.  The S^T accumulator holds per lane
-//    one query and 16 keys, which is directly P's B-operand layout; V^T's A
-//    operand takes the keys in the same order.
+//    K-chunks of 64 staged through LDS; the result goes through LDS once
+//    more so that K_nope is stored as [token][128] and V transposed as
+//    [128][token], both with 16-byte coalesced stores;
+//  * mha_attn_kernel: per (sequence, head, 128 queries) a flash-attention
+//    loop over 64-key tiles staged in LDS and shared by the four waves (32
+//    queries each): S^T = K Q^T (keys on the MFMA A side, the 192-wide
+//    query in registers on the B side), online softmax in the log2 domain
+//    with bf16 P, O^T += V^T P^T.  The S^T accumulator holds per lane one
+//    query and 16 keys, which is directly P's B-operand layout; V^T is
+//    stored with its keys permuted inside each group of 16 (vt_pos) so that
+//    a lane's A operand is one contiguous 16-byte read in the same order.
+// Blocks are numbered so that each XCD (every eighth workgroup id) takes a
+// contiguous range of work: the blocks of one (sequence, head) run on one
+// XCD together and share its L2 for the head's K, V and weights.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,23 +40,24 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ inline bf16x8_t load8(const __bf16* p) { return *(const bf16x8_t*)p; }
+__device__ inline i32x4_t ld16(const void* p) { return *(const i32x4_t*)p; }
+__device__ inline void st16(void* p, const i32x4_t& v) { *(i32x4_t*)p = v; }
+__device__ inline bf16x8_t lds8(const __bf16* p) { return *(const bf16x8_t*)p; }
 
-__device__ inline bf16x8_t zero8() { return bf16x8_t{}; }
+__device__ inline f32x16_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
-// Physical address of token j's 576-wide cache row, or null past the
-// sequence or for an out-of-range page.
-__device__ inline const __bf16* token_row(const MhaParams& p, int b, int j, int L) {
-  if (j >= L) return nullptr;
-  const int pg = p.block_table[(int64_t)b * p.MB + (j >> 6)];
-  if (pg < 0 || pg >= p.NB) return nullptr;
-  return p.kv + ((int64_t)pg * 64 + (j & 63)) * 576;
+// Position of key k in the stored V^T rows: inside each group of 16 keys,
+// keys 4e..4e+3 of the first half and 8+4e..8+4e+3 of the second half sit
+// next to each other (e = 0, 1), the order in which a lane holds P.
+__device__ inline int vt_pos(int k) {
+  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
 }
 
 // Sequence length clamped to the block table and to max_seq_len (the
@@ -61,71 +68,165 @@ __device__ inline int seq_len(const MhaParams& p, int b) {
   return L > p.max_len ? p.max_len : L;
 }
 
+// Work item of this workgroup: XCD x = blockIdx % 8 takes the contiguous
+// range [x * n, (x + 1) * n) of work ids, n = gridDim / 8.
+__device__ inline int64_t xcd_work_id() {
+  return (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+}
+
 // ---------------------------------------------------------------------------
-// Expansion.  Block (tile, head, sequence) of 4 waves; wave w computes output
-// rows [64 w, 64 w + 64) of [W_UK[h]; W_UV[h]] times the 32 latents of the
-// tile: D[m][token] = sum_k W[m][k] c_token[k], m on the MFMA A side, the
-// tokens on the B side.  D's lane layout: token column l % 32, rows
-// 8 (i / 4) + 4 (l / 32) + i % 4 of register i.
-__global__ void __launch_bounds__(256) mha_expand_kernel(const MhaParams p) {
-  const int b = blockIdx.z, h = blockIdx.y, j0 = blockIdx.x * 32;
+// Expansion.  Work id = ((b * H + h) * tiles + tile): block = 128 tokens of
+// sequence b times the 256 outputs of head h.  Wave (wm, wn) computes
+// outputs [128 wm, 128 wm + 128) (K_nope for wm = 0, V for wm = 1) of
+// tokens [64 wn, 64 wn + 64): D[m][token] = sum_k W[m][k] c_token[k], the
+// weights on the A side, the latents on the B side.  D's lane layout:
+// token column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4 of register i.
+constexpr int EX_TOK = kMhaTokPad;       // tokens per block
+constexpr int EX_KC = 64;                // K chunk
+constexpr int EX_P = EX_KC + 8;          // LDS row pitch of a chunk (bf16)
+constexpr int EX_OP = EX_TOK + 8;        // LDS row pitch of the epilogue tiles (bf16)
+constexpr int EX_LDS_CHUNK = (256 + EX_TOK) * EX_P;   // bf16
+constexpr int EX_LDS_OUT = 2 * 128 * EX_OP;           // bf16
+constexpr int EX_LDS = EX_LDS_CHUNK > EX_LDS_OUT ? EX_LDS_CHUNK : EX_LDS_OUT;
+
+__global__ void __launch_bounds__(256, 2) mha_expand_kernel(const MhaParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 lds[EX_LDS];
+  const int n_tiles = p.Lpad / EX_TOK;
+  const int64_t w = xcd_work_id();
+  if (w >= (int64_t)p.B * p.H * n_tiles) return;
+  const int tile = (int)(w % n_tiles);
+  const int64_t bh = w / n_tiles;
+  const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   const int L = seq_len(p, b);
-  if (j0 >= L) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int j = j0 + l32;
-  const __bf16* x = token_row(p, b, j, L);
-  const __bf16* wrow[2];
+  const int n0 = tile * EX_TOK;
+  if (n0 >= L) return;   // the attention never reads a tile past the sequence
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  __bf16* w_l = lds;                   // [256][EX_P]
+  __bf16* x_l = lds + 256 * EX_P;      // [128][EX_P]
+
+  // Staging: weight rows (tid >> 3) + 32 k, latent rows (tid >> 3) + 32 k,
+  // 16 bytes at column 8 (tid & 7) of the chunk.  Latent rows past the
+  // sequence, or on a page out of range, read as zeros, so their outputs
+  // are exactly zero.
+  const int sr = tid >> 3, sc = 8 * (tid & 7);
+  const __bf16* wrow[8];
 #pragma unroll
-  for (int c = 0; c < 2; c++) {
-    const int m = 64 * wave + 32 * c + l32;
-    wrow[c] = (m < 128 ? p.w_uk + ((int64_t)h * 128 + m) * 512 : p.w_uv + ((int64_t)h * 128 + (m - 128)) * 512);
+  for (int k = 0; k < 8; k++) {
+    const int m = sr + 32 * k;
+    wrow[k] = m < 128 ? p.w_uk + ((int64_t)h * 128 + m) * 512 : p.w_uv + ((int64_t)h * 128 + (m - 128)) * 512;
   }
-  f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll 4
-  for (int ks = 0; ks < 32; ks++) {
-    const int k = 16 * ks + 8 * hh;
-    const bf16x8_t bx = x ? load8(x + k) : zero8();
+  const __bf16* xrow[4];
 #pragma unroll
-    for (int c = 0; c < 2; c++) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load8(wrow[c] + k), bx, acc[c], 0, 0, 0);
+  for (int k = 0; k < 4; k++) {
+    const int j = n0 + sr + 32 * k;
+    const int pg = j < L ? p.block_table[(int64_t)b * p.MB + (j >> 6)] : -1;
+    xrow[k] = (pg >= 0 && pg < p.NB) ? p.kv + ((int64_t)pg * 64 + (j & 63)) * 576 : nullptr;
   }
-  // Tokens past the sequence in this tile are stored as zeros: the
-  // attention multiplies their V by zero weights, and stale workspace bytes
-  // could be NaN.
-  const bool real = j < L;
-  const int64_t bh = (int64_t)b * p.H + h;
+  i32x4_t wst[8], xst[4];
+  auto fetch = [&](int kc) {
 #pragma unroll
-  for (int c = 0; c < 2; c++) {
-    const int m0 = 64 * wave + 32 * c;
-    if (m0 < 128) {
-      __bf16* k_out = p.ws_k + (bh * p.Lpad + j) * 128 + m0;
+    for (int k = 0; k < 8; k++) wst[k] = ld16(wrow[k] + EX_KC * kc + sc);
 #pragma unroll
-      for (int a = 0; a < 4; a++) {
-        const bf16x4_t v = {(__bf16)(real ? acc[c][4 * a] : 0.f), (__bf16)(real ? acc[c][4 * a + 1] : 0.f),
-                            (__bf16)(real ? acc[c][4 * a + 2] : 0.f), (__bf16)(real ? acc[c][4 * a + 3] : 0.f)};
-        *(bf16x4_t*)(k_out + 8 * a + 4 * hh) = v;
+    for (int k = 0; k < 4; k++) xst[k] = xrow[k] ? ld16(xrow[k] + EX_KC * kc + sc) : i32x4_t{0, 0, 0, 0};
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int im = 0; im < 4; im++)
+#pragma unroll
+    for (int in = 0; in < 2; in++) acc[im][in] = f32x16_t{};
+  fetch(0);
+  for (int kc = 0; kc < 512 / EX_KC; kc++) {
+    __syncthreads();   // every wave is done with the previous chunk
+#pragma unroll
+    for (int k = 0; k < 8; k++) st16(w_l + (sr + 32 * k) * EX_P + sc, wst[k]);
+#pragma unroll
+    for (int k = 0; k < 4; k++) st16(x_l + (sr + 32 * k) * EX_P + sc, xst[k]);
+    __syncthreads();
+    if (kc + 1 < 512 / EX_KC) fetch(kc + 1);
+#pragma unroll
+    for (int ks = 0; ks < EX_KC / 16; ks++) {
+      bf16x8_t bx[2];
+#pragma unroll
+      for (int in = 0; in < 2; in++) bx[in] = lds8(x_l + (64 * wn + 32 * in + l32) * EX_P + 16 * ks + 8 * hh);
+#pragma unroll
+      for (int im = 0; im < 4; im++) {
+        const bf16x8_t a = lds8(w_l + (128 * wm + 32 * im + l32) * EX_P + 16 * ks + 8 * hh);
+#pragma unroll
+        for (int in = 0; in < 2; in++) acc[im][in] = mfma16(a, bx[in], acc[im][in]);
       }
-    } else {
-      __bf16* vt = p.ws_vt + (bh * 128 + (m0 - 128)) * p.Lpad + j;
-#pragma unroll
-      for (int i = 0; i < 16; i++)
-        vt[(int64_t)(8 * (i / 4) + 4 * hh + i % 4) * p.Lpad] = (__bf16)(real ? acc[c][i] : 0.f);
     }
+  }
+
+  // Epilogue: K_nope to k_l[token][dim], V to v_l[dim][vt_pos(token)], then
+  // 16-byte rows out.
+  __syncthreads();
+  __bf16* k_l = lds;                   // [128 tokens][EX_OP]
+  __bf16* v_l = lds + 128 * EX_OP;     // [128 dims][EX_OP]
+#pragma unroll
+  for (int im = 0; im < 4; im++)
+#pragma unroll
+    for (int in = 0; in < 2; in++) {
+      const int n = 64 * wn + 32 * in + l32;
+      if (wm == 0) {
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+          const bf16x4_t v = {(__bf16)acc[im][in][4 * a], (__bf16)acc[im][in][4 * a + 1],
+                              (__bf16)acc[im][in][4 * a + 2], (__bf16)acc[im][in][4 * a + 3]};
+          *(bf16x4_t*)(k_l + n * EX_OP + 32 * im + 8 * a + 4 * hh) = v;
+        }
+      } else {
+        const int pos = vt_pos(n);
+#pragma unroll
+        for (int i = 0; i < 16; i++) v_l[(32 * im + 8 * (i / 4) + 4 * hh + i % 4) * EX_OP + pos] = (__bf16)acc[im][in][i];
+      }
+    }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const int q = tid + 256 * k, r = q >> 4, c = 8 * (q & 15);
+    st16(p.ws_k + ((bh * p.Lpad) + n0 + r) * 128 + c, ld16(k_l + r * EX_OP + c));
+    st16(p.ws_vt + (bh * 128 + r) * p.Lpad + n0 + c, ld16(v_l + r * EX_OP + c));
   }
 }
 
 // ---------------------------------------------------------------------------
-// Attention.  One wave per (32-query block, head, sequence).
-__global__ void __launch_bounds__(64) mha_attn_kernel(const MhaParams p) {
-  const int b = blockIdx.z, h = blockIdx.y, t0 = blockIdx.x * 32;
+// Attention.  Work id = (b * H + h) * chunks + (chunks - 1 - chunk): the
+// blocks of one (sequence, head) run together on one XCD, the longest
+// (last) query chunk first.  Wave w takes queries q0 + 32 w + (lane % 32).
+constexpr int AT_Q = 128;                // queries per block
+constexpr int AT_KT = 64;                // keys per tile
+constexpr int AT_KP = 192 + 8;           // LDS pitch of a key row (bf16)
+constexpr int AT_VP = AT_KT + 8;         // LDS pitch of a V^T row (bf16)
+
+__global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 k_l[AT_KT * AT_KP];
+  __shared__ __attribute__((aligned(16))) __bf16 v_l[128 * AT_VP];
+  const int n_qc = (p.T + AT_Q - 1) / AT_Q;
+  const int64_t w = xcd_work_id();
+  if (w >= (int64_t)p.B * p.H * n_qc) return;
+  const int qc = n_qc - 1 - (int)(w % n_qc);
+  const int64_t bh = w / n_qc;
+  const int h = (int)(bh % p.H), b = (int)(bh / p.H);
   const int L = seq_len(p, b);
-  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
-  const int t = t0 + l32;
+  const int q0 = qc * AT_Q;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int t = q0 + 32 * wave + l32;
   const bool t_ok = t < p.T;
   const int n_vis = t_ok ? max(0, L - p.T + t + 1) : 0;   // keys this lane's query sees
-  int nv_max = n_vis;
+  // Keys the wave needs at most, and the fewest any of its real queries
+  // sees (tiles below that need no mask).
+  int nv_max = n_vis, nv_min = t_ok ? n_vis : 0x7fffffff;
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) nv_max = max(nv_max, __shfl_xor(nv_max, d));
+  for (int d = 32; d >= 1; d >>= 1) {
+    nv_max = max(nv_max, __shfl_xor(nv_max, d));
+    nv_min = min(nv_min, __shfl_xor(nv_min, d));
+  }
+  const int t_last = min(q0 + AT_Q, p.T) - 1;
+  const int n_blk = max(0, L - p.T + t_last + 1);   // keys the block needs
+  const int n_kt = (n_blk + AT_KT - 1) / AT_KT;
 
   // Query operand: B side, column = query, 8 features per lane half and step.
   bf16x8_t qreg[12];
@@ -134,75 +235,116 @@ __global__ void __launch_bounds__(64) mha_attn_kernel(const MhaParams p) {
 #pragma unroll
     for (int ks = 0; ks < 12; ks++) {
       const int k = 16 * ks + 8 * hh;
-      const bf16x8_t v = ks < 8 ? load8(p.q_nope + qr * 128 + k) : load8(p.q_pe + qr * 64 + (k - 128));
-      qreg[ks] = t_ok ? v : zero8();
+      const bf16x8_t v = ks < 8 ? lds8(p.q_nope + qr * 128 + k) : lds8(p.q_pe + qr * 64 + (k - 128));
+      qreg[ks] = t_ok ? v : bf16x8_t{};
     }
   }
+
+  // Staging of one tile (16-byte pieces): K_nope rows tid / 16 + 16 k
+  // (columns 8 (tid % 16)), rope rows tid / 8 + 32 k (columns 8 (tid % 8)),
+  // V^T rows tid / 8 + 32 k (keys 8 (tid % 8)).  The tile's keys all lie on
+  // one page of the cache.  Every tile read starts below L, inside a
+  // 128-token block the expansion wrote (zeros past L), so the workspace
+  // reads need no bounds.
+  i32x4_t kst[4], rst[2], vst[4];
+  const __bf16* ks_base = p.ws_k + bh * p.Lpad * 128;
+  const __bf16* vt_base = p.ws_vt + bh * 128 * p.Lpad;
+  auto fetch = [&](int j0) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int q = tid + 256 * k;
+      kst[k] = ld16(ks_base + (int64_t)(j0 + (q >> 4)) * 128 + 8 * (q & 15));
+      vst[k] = ld16(vt_base + (int64_t)(q >> 3) * p.Lpad + j0 + 8 * (q & 7));
+    }
+    const int pg = p.block_table[(int64_t)b * p.MB + (j0 >> 6)];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int q = tid + 256 * k, r = q >> 3;
+      rst[k] = (j0 + r < L && pg >= 0 && pg < p.NB)
+                   ? ld16(p.kv + ((int64_t)pg * 64 + r) * 576 + 512 + 8 * (q & 7))
+                   : i32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int q = tid + 256 * k;
+      st16(k_l + (q >> 4) * AT_KP + 8 * (q & 15), kst[k]);
+      st16(v_l + (q >> 3) * AT_VP + 8 * (q & 7), vst[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int q = tid + 256 * k;
+      st16(k_l + (q >> 3) * AT_KP + 128 + 8 * (q & 7), rst[k]);
+    }
+  };
+
   const float c_qk = p.qk_scale;   // softmax scale * log2(e)
   float m = -INFINITY;             // running maximum (log2 domain), per query
   float l = 0.f;                   // this half's sum of the rounded weights
   f32x16_t o[4] = {f32x16_t{}, f32x16_t{}, f32x16_t{}, f32x16_t{}};   // O^T, dims 32 f .. 32 f + 31
-  const int64_t bh = (int64_t)b * p.H + h;
-  const __bf16* ks_base = p.ws_k + bh * p.Lpad * 128;
-  const __bf16* vt_base = p.ws_vt + bh * 128 * p.Lpad;
   const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
 
-  for (int j0 = 0; j0 < nv_max; j0 += 32) {
-    // K tile on the A side: row = key j0 + l32; K_nope from the workspace,
-    // the rope part from the cache.
-    const int j = j0 + l32;
-    const __bf16* rope = token_row(p, b, j, L);
-    const bool j_ok = j < L;
-    f32x16_t s = f32x16_t{};
+  if (n_kt > 0) fetch(0);
+  for (int kt = 0; kt < n_kt; kt++) {
+    const int j0 = kt * AT_KT;
+    __syncthreads();   // every wave is done with the previous tile
+    store();
+    __syncthreads();
+    if (kt + 1 < n_kt) fetch(j0 + AT_KT);
+    if (j0 >= nv_max) continue;   // no query of this wave sees the tile
+
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-    for (int ks = 0; ks < 12; ks++) {
-      const int k = 16 * ks + 8 * hh;
-      bf16x8_t a;
-      if (ks < 8) a = j_ok ? load8(ks_base + (int64_t)j * 128 + k) : zero8();
-      else a = rope ? load8(rope + 512 + (k - 128)) : zero8();
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s, 0, 0, 0);
-    }
-    // Register i holds key j0 + 8 (i / 4) + 4 hh + i % 4 of this lane's query.
-    float x[16];
+    for (int ks = 0; ks < 12; ks++)
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+        s[kb] = mfma16(lds8(k_l + (32 * kb + l32) * AT_KP + 16 * ks + 8 * hh), qreg[ks], s[kb]);
+
+    // Register i of block kb holds key j0 + 32 kb + 8 (i / 4) + 4 hh + i % 4.
+    const bool masked = j0 + AT_KT > nv_min;
     float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int key = j0 + 8 * (i / 4) + 4 * hh + (i % 4);
-      x[i] = key < n_vis ? s[i] * c_qk : -INFINITY;
-      tmax = fmaxf(tmax, x[i]);
-    }
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        float x = s[kb][i] * c_qk;
+        if (masked && j0 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= n_vis) x = -INFINITY;
+        s[kb][i] = x;
+        tmax = fmaxf(tmax, x);
+      }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m, tmax);
     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
     const float sh = m_new == -INFINITY ? 0.f : m_new;
-    bf16x8_t pb[2];
+    bf16x8_t pb[2][2];
     float ls = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const bf16x2_t pr = {(__bf16)__builtin_amdgcn_exp2f(x[i] - sh), (__bf16)__builtin_amdgcn_exp2f(x[i + 1] - sh)};
-      ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
-      pb[i / 8][i % 8] = pr[0];
-      pb[i / 8][i % 8 + 1] = pr[1];
-    }
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const bf16x2_t pr = {(__bf16)__builtin_amdgcn_exp2f(s[kb][i] - sh),
+                             (__bf16)__builtin_amdgcn_exp2f(s[kb][i + 1] - sh)};
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
+        pb[kb][i / 8][i % 8] = pr[0];
+        pb[kb][i / 8][i % 8 + 1] = pr[1];
+      }
     l = l * alpha + ls;
     m = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int f = 0; f < 4; f++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) o[f][i] *= alpha;
+    }
+    // V^T on the A side: row = dim 32 f + l32, keys 16 s + [8 hh, 8 hh + 8)
+    // in stored order, which is the order of P's group s (block s / 2,
+    // registers 8 (s % 2) ..).
 #pragma unroll
     for (int f = 0; f < 4; f++)
 #pragma unroll
-      for (int i = 0; i < 16; i++) o[f][i] *= alpha;
-    // V^T on the A side: row = dim 32 f + l32; step s2 takes keys
-    // 16 s2 + 4 hh + {0..3} and 16 s2 + 8 + 4 hh + {0..3}, the order of pb.
-#pragma unroll
-    for (int f = 0; f < 4; f++) {
-      const __bf16* vrow = vt_base + (int64_t)(32 * f + l32) * p.Lpad + j0;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; s2++) {
-        const i32x2_t lo = *(const i32x2_t*)(vrow + 16 * s2 + 4 * hh);
-        const i32x2_t hi = *(const i32x2_t*)(vrow + 16 * s2 + 8 + 4 * hh);
-        const i32x4_t cat = {lo[0], lo[1], hi[0], hi[1]};
-        o[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cat), pb[s2], o[f], 0, 0, 0);
-      }
-    }
+      for (int s4 = 0; s4 < 4; s4++)
+        o[f] = mfma16(lds8(v_l + (32 * f + l32) * AT_VP + 16 * s4 + 8 * hh), pb[s4 >> 1][s4 & 1], o[f]);
   }
 
   const float l_tot = l + __shfl_xor(l, 32);
@@ -228,17 +370,20 @@ __global__ void __launch_bounds__(64) mha_attn_kernel(const MhaParams p) {
   if (hh == 0 && p.lse) p.lse[orow] = empty ? -INFINITY : (m + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
+unsigned grid_of(int64_t work) { return (unsigned)((work + 7) / 8 * 8); }
+
 }  // namespace
 
 hipError_t launch_mha(const MhaParams& p, hipStream_t stream) {
   void* args[] = {(void*)&p};
   if (p.Lpad > 0) {   // no cached token at all: the attention alone writes the empty rows
-    const dim3 ge((unsigned)(p.Lpad / 32), (unsigned)p.H, (unsigned)p.B);
-    const hipError_t e = hipLaunchKernel((const void*)&mha_expand_kernel, ge, dim3(256), args, 0, stream);
+    const int64_t work = (int64_t)p.B * p.H * (p.Lpad / EX_TOK);
+    const hipError_t e = hipLaunchKernel((const void*)&mha_expand_kernel, dim3(grid_of(work)), dim3(256), args, 0,
+                                         stream);
     if (e != hipSuccess) return e;
   }
-  const dim3 ga((unsigned)((p.T + 31) / 32), (unsigned)p.H, (unsigned)p.B);
-  return hipLaunchKernel((const void*)&mha_attn_kernel, ga, dim3(64), args, 0, stream);
+  const int64_t work = (int64_t)p.B * p.H * ((p.T + AT_Q - 1) / AT_Q);
+  return hipLaunchKernel((const void*)&mha_attn_kernel, dim3(grid_of(work)), dim3(256), args, 0, stream);
 }
 
 }  // namespace mla

@@ -111,7 +111,8 @@ hipError_t launch_merge_kernel(const MergeParams& m, hipStream_t) {
 
 hipError_t launch_mha(const MhaParams& p, hipStream_t) {
   g_mha_launches++;
-  CHECK(p.Lpad % 32 == 0 && p.Lpad >= p.max_len && p.Lpad < p.max_len + 32, "Lpad %d for %d", p.Lpad, p.max_len);
+  CHECK(p.Lpad % kMhaTokPad == 0 && p.Lpad >= p.max_len && p.Lpad < p.max_len + kMhaTokPad, "Lpad %d for %d",
+        p.Lpad, p.max_len);
   CHECK(p.Lpad == 0 || (p.ws_k != nullptr && p.ws_vt != nullptr), "mha workspace");
   CHECK((char*)p.ws_vt - (char*)p.ws_k == (ptrdiff_t)((size_t)p.B * p.H * p.Lpad * 128 * 2), "V^T offset");
   return hipSuccess;

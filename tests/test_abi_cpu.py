@@ -278,9 +278,9 @@ def test_noalloc_refuses_partials_beyond_its_static_buffer(lib):
 
 def test_dense_mha_workspace_formula(lib):
     """K_nope [B, H, Lpad, 128] and V^T [B, H, 128, Lpad] bf16, Lpad = max_seq_len
-    rounded up to 32."""
-    for B, H, L in ((2, 16, 300), (1, 1, 1), (3, 128, 8192), (4, 8, 0), (1, 2, 32)):
-        lpad = (L + 31) // 32 * 32
+    rounded up to 128."""
+    for B, H, L in ((2, 16, 300), (1, 1, 1), (3, 128, 8192), (4, 8, 0), (1, 2, 128), (1, 2, 129)):
+        lpad = (L + 127) // 128 * 128
         assert binding.dense_mha_workspace_size(B, H, L) == 2 * B * H * lpad * 128 * 2
     assert binding.dense_mha_workspace_size(-1, 16, 100) == 0
     assert binding.dense_mha_workspace_size(1, 0, 100) == 0
@@ -307,7 +307,8 @@ def _call_mha(lib, **kw):
     (dict(odt=3), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(MB=0), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("inf")), binding.MLA_ERR_INVALID_ARGUMENT),
-    (dict(wsb=2 * 2 * 16 * 320 * 128 * 2 - 1), binding.MLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(wsb=2 * 2 * 16 * 384 * 128 * 2 - 1), binding.MLA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(B=65535, H=1024, msl=1 << 24, wsb=1 << 62), binding.MLA_ERR_UNSUPPORTED),
     (dict(ws=None), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(ws=FAKE + 8), binding.MLA_ERR_INVALID_ARGUMENT),
 ])
