@@ -29,29 +29,34 @@ def _device_asm_cmd(out: str, src: str):
     return [HIPCC] + flags + ["--offload-device-only", "-S", "-o", out, src]
 
 
-def _build_one(lib: str, sources, scanned: str, verbose: bool) -> str:
+def _build_one(lib: str, sources, scanned, verbose: bool) -> str:
+    """Compile `sources` into `lib`; the device assembly of each file in
+    `scanned` is checked for hazards before inline-asm memory instructions."""
     from mla_paged_latent_03_amd import asm_hazards
 
     tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + ["-o", tmp] + sources
     if verbose:
         print(" ".join(cmd), flush=True)
+    found = []
     with tempfile.TemporaryDirectory() as td:
-        asm_path = os.path.join(td, "kernels.s")
-        asm_proc = subprocess.Popen(_device_asm_cmd(asm_path, scanned), stdout=subprocess.DEVNULL,
-                                    stderr=subprocess.PIPE, text=True)
+        asm_paths = [os.path.join(td, "kernels%d.s" % i) for i in range(len(scanned))]
+        asm_procs = [subprocess.Popen(_device_asm_cmd(a, src), stdout=subprocess.DEVNULL, stderr=subprocess.PIPE,
+                                      text=True) for a, src in zip(asm_paths, scanned)]
         res = subprocess.run(cmd, capture_output=True, text=True)
-        asm_err = asm_proc.communicate()[1]
+        asm_errs = [pr.communicate()[1] for pr in asm_procs]
         noise = ("packed-fp32-ops", "unknown target feature")
         err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in noise))
         if res.returncode != 0:
             raise RuntimeError("hipcc failed:\n" + err)
-        if asm_proc.returncode != 0:
-            raise RuntimeError("hipcc (device assembly) failed:\n" + asm_err)
+        for pr, e in zip(asm_procs, asm_errs):
+            if pr.returncode != 0:
+                raise RuntimeError("hipcc (device assembly) failed:\n" + e)
         if err.strip() and verbose:
             print(err, file=sys.stderr)
-        with open(asm_path) as f:
-            found = asm_hazards.scan(f.read())
+        for a, src in zip(asm_paths, scanned):
+            with open(a) as f:
+                found += ["%s: %s" % (os.path.basename(src), x) for x in asm_hazards.scan(f.read())]
     if found:
         os.remove(tmp)
         raise RuntimeError("hazards before inline-asm memory instructions:\n" + "\n".join(found[:20]))
@@ -63,8 +68,8 @@ def build(verbose: bool = False) -> str:
     """Compile the decode library and the benchmark's streaming-read
     reference, each with its kernels' gfx950 assembly alongside; fail if the
     assembly shows a hazard before an inline-asm memory instruction."""
-    _build_one(STREAM_LIB, [STREAM_SRC], STREAM_SRC, verbose)
-    return _build_one(LIB, SOURCES, SOURCES[0], verbose)
+    _build_one(STREAM_LIB, [STREAM_SRC], [STREAM_SRC], verbose)
+    return _build_one(LIB, SOURCES, [f for f in SOURCES if f.endswith(".hip")], verbose)
 
 
 if __name__ == "__main__":

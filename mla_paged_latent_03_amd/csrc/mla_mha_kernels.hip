@@ -49,6 +49,21 @@ __device__ inline i32x4_t ld16(const void* p) { return *(const i32x4_t*)p; }
 __device__ inline void st16(void* p, const i32x4_t& v) { *(i32x4_t*)p = v; }
 __device__ inline bf16x8_t lds8(const __bf16* p) { return *(const bf16x8_t*)p; }
 
+// Sixteen zero bytes: the source of DMA lanes with nothing to load.
+__device__ __attribute__((aligned(16))) uint8_t g_mha_zero16[16];
+
+// LDS DMA: lane i copies 16 bytes from gsrc_i to LDS bytes [m0 + 16 i,
+// m0 + 16 i + 16).  Issued from inline asm, so the compiler neither waits
+// for it nor counts it; the kernel waits with vmcnt(0) before the barrier
+// that publishes the tile.  The s_nop gives the one wait state an LDS DMA
+// needs after the SALU write of M0 that precedes it (the compiler adds none
+// before inline asm); the build scans the compiled kernels for it.
+__device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(lds_byte_addr) : "memory");
+}
+
+__device__ inline void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ inline f32x16_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -196,14 +211,24 @@ __global__ void __launch_bounds__(256, 2) mha_expand_kernel(const MhaParams p) {
 // Attention.  Work id = (b * H + h) * chunks + (chunks - 1 - chunk): the
 // blocks of one (sequence, head) run together on one XCD, the longest
 // (last) query chunk first.  Wave w takes queries q0 + 32 w + (lane % 32).
+// Two tile buffers in LDS: while the waves compute on one, the next tile
+// streams into the other by LDS DMA, one barrier per tile.  A buffer holds
+// the tile's K_nope rows (64 x 256 B), rope rows (64 x 128 B) and V^T rows
+// (128 x 128 B), unpadded, their 16-byte pieces XOR-swizzled (swz16 for the
+// 16-piece rows, swz8 for the 8-piece ones) so that the 16 lanes of a
+// 16-byte LDS read always hit 16 distinct bank quads.
 constexpr int AT_Q = 128;                // queries per block
 constexpr int AT_KT = 64;                // keys per tile
-constexpr int AT_KP = 192 + 8;           // LDS pitch of a key row (bf16)
-constexpr int AT_VP = AT_KT + 8;         // LDS pitch of a V^T row (bf16)
+constexpr int AT_NOPE = AT_KT * 128;     // bf16 of the K_nope rows
+constexpr int AT_ROPE = AT_KT * 64;      // bf16 of the rope rows
+constexpr int AT_VT = 128 * AT_KT;       // bf16 of the V^T rows
+constexpr int AT_BUF = AT_NOPE + AT_ROPE + AT_VT;   // one tile buffer (40 KiB)
+
+__device__ inline int swz16(int row, int c) { return c ^ (row & 15); }
+__device__ inline int swz8(int row, int c) { return c ^ ((row >> 1) & 7); }
 
 __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 k_l[AT_KT * AT_KP];
-  __shared__ __attribute__((aligned(16))) __bf16 v_l[128 * AT_VP];
+  __shared__ __attribute__((aligned(16))) __bf16 tbuf[2 * AT_BUF];
   const int n_qc = (p.T + AT_Q - 1) / AT_Q;
   const int64_t w = xcd_work_id();
   if (w >= (int64_t)p.B * p.H * n_qc) return;
@@ -240,43 +265,56 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
     }
   }
 
-  // Staging of one tile (16-byte pieces): K_nope rows tid / 16 + 16 k
-  // (columns 8 (tid % 16)), rope rows tid / 8 + 32 k (columns 8 (tid % 8)),
-  // V^T rows tid / 8 + 32 k (keys 8 (tid % 8)).  The tile's keys all lie on
-  // one page of the cache.  Every tile read starts below L, inside a
-  // 128-token block the expansion wrote (zeros past L), so the workspace
-  // reads need no bounds.
-  i32x4_t kst[4], rst[2], vst[4];
+  // One tile goes from HBM into a buffer by 40 LDS-DMA instructions of 64
+  // lanes; instruction g fills 16-byte slots [64 g, 64 g + 64) of the
+  // buffer: g < 16 the K_nope rows, g < 24 the rope rows (from the cache),
+  // the rest the V^T rows.  Wave w issues K_nope instructions 4 w .. 4 w + 3,
+  // rope 16 + 2 w, 17 + 2 w and V^T 24 + 4 w .. 27 + 4 w, so the kind of its
+  // i-th instruction is fixed at compile time.  A slot's logical piece is
+  // its swizzled position (each swizzle is its own inverse), so every lane's
+  // source offset within a tile is fixed and only the tile start moves.
+  // The tile's keys all lie on one cache page, looked up one tile ahead (a
+  // page out of range reads zeros).  Every tile read starts below L, inside
+  // a 128-token block the expansion wrote (zeros past L), so the workspace
+  // reads need no bounds; rope rows past L are read from their page and
+  // masked out of the softmax.
   const __bf16* ks_base = p.ws_k + bh * p.Lpad * 128;
   const __bf16* vt_base = p.ws_vt + bh * 128 * p.Lpad;
-  auto fetch = [&](int j0) {
+  const int32_t* bt = p.block_table + (int64_t)b * p.MB;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int src_off[10];    // element offset of this lane's piece within the tile's source
+  uint32_t dst[10];   // LDS byte offset of the instruction within a buffer
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const int q = tid + 256 * k;
-      kst[k] = ld16(ks_base + (int64_t)(j0 + (q >> 4)) * 128 + 8 * (q & 15));
-      vst[k] = ld16(vt_base + (int64_t)(q >> 3) * p.Lpad + j0 + 8 * (q & 7));
+  for (int i = 0; i < 10; i++) {
+    if (i < 4) {
+      const int g = 4 * wv + i, sl = 64 * g + lane, r = sl >> 4;
+      src_off[i] = r * 128 + 8 * swz16(r, sl & 15);
+      dst[i] = g * 1024;
+    } else if (i < 6) {
+      const int g = 16 + 2 * wv + (i - 4), sl = 64 * (g - 16) + lane, r = sl >> 3;
+      src_off[i] = r * 576 + 512 + 8 * swz8(r, sl & 7);
+      dst[i] = g * 1024;
+    } else {
+      const int g = 24 + 4 * wv + (i - 6), sl = 64 * (g - 24) + lane, d = sl >> 3;
+      src_off[i] = d * p.Lpad + 8 * swz8(d, sl & 7);
+      dst[i] = g * 1024;
     }
-    const int pg = p.block_table[(int64_t)b * p.MB + (j0 >> 6)];
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)tbuf;
+  int pg = n_kt > 0 ? bt[0] : -1;   // page of the next tile to fetch
+  auto fetch = [&](int j0, int buf) {
+    const int pgu = __builtin_amdgcn_readfirstlane(pg);
+    const bool pg_ok = pgu >= 0 && pgu < p.NB;
+    const uint32_t lb = lds0 + (uint32_t)(buf * AT_BUF * 2);
 #pragma unroll
-    for (int k = 0; k < 2; k++) {
-      const int q = tid + 256 * k, r = q >> 3;
-      rst[k] = (j0 + r < L && pg >= 0 && pg < p.NB)
-                   ? ld16(p.kv + ((int64_t)pg * 64 + r) * 576 + 512 + 8 * (q & 7))
-                   : i32x4_t{0, 0, 0, 0};
+    for (int i = 0; i < 10; i++) {
+      const void* src;
+      if (i < 4) src = ks_base + (int64_t)j0 * 128 + src_off[i];
+      else if (i < 6) src = pg_ok ? (const void*)(p.kv + (int64_t)pgu * 64 * 576 + src_off[i]) : (const void*)g_mha_zero16;
+      else src = vt_base + j0 + src_off[i];
+      dma16(src, lb + dst[i]);
     }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const int q = tid + 256 * k;
-      st16(k_l + (q >> 4) * AT_KP + 8 * (q & 15), kst[k]);
-      st16(v_l + (q >> 3) * AT_VP + 8 * (q & 7), vst[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      const int q = tid + 256 * k;
-      st16(k_l + (q >> 3) * AT_KP + 128 + 8 * (q & 7), rst[k]);
-    }
+    pg = j0 + AT_KT < n_blk ? bt[(j0 + AT_KT) >> 6] : -1;
   };
 
   const float c_qk = p.qk_scale;   // softmax scale * log2(e)
@@ -285,66 +323,77 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
   f32x16_t o[4] = {f32x16_t{}, f32x16_t{}, f32x16_t{}, f32x16_t{}};   // O^T, dims 32 f .. 32 f + 31
   const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
 
-  if (n_kt > 0) fetch(0);
+  if (n_kt > 0) fetch(0, 0);
+  if (n_kt > 1) fetch(AT_KT, 1);
+  wait_vmcnt0();
+  __syncthreads();
   for (int kt = 0; kt < n_kt; kt++) {
     const int j0 = kt * AT_KT;
-    __syncthreads();   // every wave is done with the previous tile
-    store();
-    __syncthreads();
-    if (kt + 1 < n_kt) fetch(j0 + AT_KT);
-    if (j0 >= nv_max) continue;   // no query of this wave sees the tile
-
-    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+    const __bf16* kn_l = tbuf + (kt & 1) * AT_BUF;   // K_nope rows
+    const __bf16* kr_l = kn_l + AT_NOPE;               // rope rows
+    const __bf16* vb_l = kr_l + AT_ROPE;               // V^T rows
+    if (j0 < nv_max) {   // some query of this wave sees the tile
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-    for (int ks = 0; ks < 12; ks++)
+      for (int ks = 0; ks < 12; ks++)
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+          const int r = 32 * kb + l32;
+          const __bf16* a = ks < 8 ? kn_l + (r * 16 + swz16(r, 2 * ks + hh)) * 8
+                                   : kr_l + (r * 8 + swz8(r, 2 * (ks - 8) + hh)) * 8;
+          s[kb] = mfma16(lds8(a), qreg[ks], s[kb]);
+        }
+
+      // Register i of block kb holds key j0 + 32 kb + 8 (i / 4) + 4 hh + i % 4.
+      const bool masked = j0 + AT_KT > nv_min;
+      float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
-        s[kb] = mfma16(lds8(k_l + (32 * kb + l32) * AT_KP + 16 * ks + 8 * hh), qreg[ks], s[kb]);
-
-    // Register i of block kb holds key j0 + 32 kb + 8 (i / 4) + 4 hh + i % 4.
-    const bool masked = j0 + AT_KT > nv_min;
-    float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
+        for (int i = 0; i < 16; i++) {
+          float x = s[kb][i] * c_qk;
+          if (masked && j0 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= n_vis) x = -INFINITY;
+          s[kb][i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m, tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+      const float sh = m_new == -INFINITY ? 0.f : m_new;
+      bf16x8_t pb[2][2];
+      float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        float x = s[kb][i] * c_qk;
-        if (masked && j0 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= n_vis) x = -INFINITY;
-        s[kb][i] = x;
-        tmax = fmaxf(tmax, x);
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const bf16x2_t pr = {(__bf16)__builtin_amdgcn_exp2f(s[kb][i] - sh),
+                               (__bf16)__builtin_amdgcn_exp2f(s[kb][i + 1] - sh)};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
+          pb[kb][i / 8][i % 8] = pr[0];
+          pb[kb][i / 8][i % 8 + 1] = pr[1];
+        }
+      l = l * alpha + ls;
+      m = m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int f = 0; f < 4; f++)
+#pragma unroll
+          for (int i = 0; i < 16; i++) o[f][i] *= alpha;
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-    const float sh = m_new == -INFINITY ? 0.f : m_new;
-    bf16x8_t pb[2][2];
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const bf16x2_t pr = {(__bf16)__builtin_amdgcn_exp2f(s[kb][i] - sh),
-                             (__bf16)__builtin_amdgcn_exp2f(s[kb][i + 1] - sh)};
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
-        pb[kb][i / 8][i % 8] = pr[0];
-        pb[kb][i / 8][i % 8 + 1] = pr[1];
-      }
-    l = l * alpha + ls;
-    m = m_new;
-    if (__any(alpha != 1.f)) {
+      // V^T on the A side: row = dim 32 f + l32, keys 16 s + [8 hh, 8 hh + 8)
+      // in stored order, which is the order of P's group s (block s / 2,
+      // registers 8 (s % 2) ..).
 #pragma unroll
       for (int f = 0; f < 4; f++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) o[f][i] *= alpha;
+        for (int s4 = 0; s4 < 4; s4++) {
+          const int d = 32 * f + l32;
+          o[f] = mfma16(lds8(vb_l + (d * 8 + swz8(d, 2 * s4 + hh)) * 8), pb[s4 >> 1][s4 & 1], o[f]);
+        }
     }
-    // V^T on the A side: row = dim 32 f + l32, keys 16 s + [8 hh, 8 hh + 8)
-    // in stored order, which is the order of P's group s (block s / 2,
-    // registers 8 (s % 2) ..).
-#pragma unroll
-    for (int f = 0; f < 4; f++)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; s4++)
-        o[f] = mfma16(lds8(v_l + (32 * f + l32) * AT_VP + 16 * s4 + 8 * hh), pb[s4 >> 1][s4 & 1], o[f]);
+    wait_vmcnt0();     // this wave's DMAs of tile kt + 1 have landed
+    __syncthreads();   // tile kt + 1 complete; every wave is done with tile kt's buffer
+    if (kt + 2 < n_kt) fetch(j0 + 2 * AT_KT, kt & 1);
   }
 
   const float l_tot = l + __shfl_xor(l, 32);
