@@ -1793,22 +1793,46 @@ mla_partial_kernel(const PartialParams p) {
                            acc[f][4 * a4 + 3] * iv};
         *(LDS_AS f32x4_t*)(stg + l32 * kStgStride + 32 * f + 8 * a4 + 4 * h) = v;
       }
-    // Eight rows at a time: their sixteen LDS reads go out together, so the
-    // read latency is paid once per group rather than once per row.
+    if (!FS && !p.fused) {
+      // Two rows per store instruction, 16 bytes per lane: lane l writes
+      // features 4 (l % 32) .. + 3 of row 2 k + l / 32 of each group of
+      // eight.  A partial row starts 4-byte aligned (513 floats), which the
+      // 16-byte global stores accept; the LDS reads are 16-byte aligned.
+      typedef float f32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
+      typedef float f32x4_t __attribute__((ext_vector_type(4)));
+      const int hr = lane >> 5, c4 = 4 * (lane & 31);
 #pragma unroll
-    for (int r0 = 0; r0 < 32; r0 += 8) {
-      float v[16];
+      for (int r0 = 0; r0 < 32; r0 += 8) {
+        f32x4_t v[4];
 #pragma unroll
-      for (int k = 0; k < 8; k++) {
-        v[2 * k] = stg[(r0 + k) * kStgStride + lane];
-        v[2 * k + 1] = stg[(r0 + k) * kStgStride + 64 + lane];
+        for (int k = 0; k < 4; k++) v[k] = *(const LDS_AS f32x4_t*)(stg + (r0 + 2 * k + hr) * kStgStride + c4);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const int r = r0 + 2 * k + hr;
+          if ((ok >> r) & 1u) {
+            f32x4a4_t* w = (f32x4a4_t*)(p.ws + ((qr0 + r) * p.S + split) * (int64_t)kPartialWidth + fbase + c4);
+            *w = f32x4a4_t{v[k][0], v[k][1], v[k][2], v[k][3]};
+          }
+        }
       }
+    } else {
+      // Eight rows at a time: their sixteen LDS reads go out together, so the
+      // read latency is paid once per group rather than once per row.
 #pragma unroll
-      for (int k = 0; k < 8; k++) {
-        if ((ok >> (r0 + k)) & 1u) {
-          float* w = p.ws + ((qr0 + r0 + k) * p.S + split) * (int64_t)kPartialWidth + fbase;
-          put(&w[lane], v[2 * k]);
-          put(&w[64 + lane], v[2 * k + 1]);
+      for (int r0 = 0; r0 < 32; r0 += 8) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          v[2 * k] = stg[(r0 + k) * kStgStride + lane];
+          v[2 * k + 1] = stg[(r0 + k) * kStgStride + 64 + lane];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          if ((ok >> (r0 + k)) & 1u) {
+            float* w = p.ws + ((qr0 + r0 + k) * p.S + split) * (int64_t)kPartialWidth + fbase;
+            put(&w[lane], v[2 * k]);
+            put(&w[64 + lane], v[2 * k + 1]);
+          }
         }
       }
     }
@@ -1943,8 +1967,8 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(const MergeParams p) {
       // Eight splits at a time: all of a group's loads are issued before any
       // is used, so their latencies overlap.  A split of weight zero (an
       // empty one, lse -inf) is not read: its outputs may be undefined.
-      // (Rows of 513 floats are only 4-byte aligned, hence single-float
-      // loads.)
+      // Rows of 513 floats are only 4-byte aligned; the 16-byte global loads
+      // accept that.
       const int ns = min(64, p.S - s0);
       for (int k0 = 0; k0 < ns; k0 += 8) {
         float wk[8];
@@ -1954,9 +1978,14 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(const MergeParams p) {
 #pragma unroll
         for (int k = 0; k < 8; k++) {
           if (wk[k] != 0.f) {
-            const float* src = base + (int64_t)(s0 + k0 + k) * kPartialWidth + 8 * lane;
+            typedef float f32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
+            const f32x4a4_t* src = (const f32x4a4_t*)(base + (int64_t)(s0 + k0 + k) * kPartialWidth + 8 * lane);
+            const f32x4a4_t lo = src[0], hi = src[1];
 #pragma unroll
-            for (int c = 0; c < 8; c++) v[k][c] = src[c];
+            for (int c = 0; c < 4; c++) {
+              v[k][c] = lo[c];
+              v[k][4 + c] = hi[c];
+            }
           }
         }
 #pragma unroll
