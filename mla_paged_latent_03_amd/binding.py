@@ -258,3 +258,46 @@ def decode(inp, num_kv_splits=0, out=None, lse=None, workspace=None, stream=None
         mla_decode(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, msl, inp.softmax_scale, out,
                    lse, workspace, num_kv_splits, stream)
     return out, lse, workspace
+
+
+def prepare_decode(inp, num_kv_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """The entry point that matches ``inp`` with its arguments marshalled once:
+    returns a callable that makes the same C call each time it is invoked
+    (for timing loops, where per-call marshalling would show up as host time).
+    out = lse = None runs the first stage only, as the entry points do."""
+    lib = load()
+    B, T, H = inp.B, inp.T, inp.H
+    NB, P, _ = inp.kv_cache.shape
+    MB = inp.block_table.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    fp8 = inp.kv_dtype == "fp8"
+    head = [_ptr(inp.q_nope), _ptr(inp.q_pe), _ptr(inp.kv_cache), _ptr(inp.block_table), _ptr(inp.seq_lens)]
+    scales = [float(inp.q_scale), float(inp.kv_scale)] if fp8 else []
+    dims = [B, T, H, NB, P, MB, int(inp.max_seq_len), float(inp.softmax_scale)]
+    tail = [_ptr(out), _out_code(out), _ptr(lse), _ptr(workspace), ws_bytes, int(num_kv_splits), _stream(stream)]
+    if inp.K > 0:
+        fn = lib.mla_sparse_decode_fp8 if fp8 else lib.mla_sparse_decode
+        args = head + [_ptr(inp.topk_indices), inp.K] + dims + scales + tail
+    else:
+        fn = lib.mla_decode_fp8 if fp8 else lib.mla_decode
+        args = head + dims + scales + tail
+    name = fn.__name__
+
+    def call():
+        st = fn(*args)
+        if st != MLA_OK:
+            raise MLAError(st, name)
+    return call
+
+
+def prepare_merge(workspace, rows, num_kv_splits, out, lse=None, stream=None):
+    """mla_merge_partials with its arguments marshalled once (see prepare_decode)."""
+    lib = load()
+    args = [_ptr(workspace), int(rows), int(num_kv_splits), _ptr(out), _out_code(out), _ptr(lse), _stream(stream)]
+
+    def call():
+        st = lib.mla_merge_partials(*args)
+        if st != MLA_OK:
+            raise MLAError(st, "mla_merge_partials")
+    return call
+

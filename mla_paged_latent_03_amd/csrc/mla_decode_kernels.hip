@@ -1245,15 +1245,18 @@ mla_partial_kernel(const PartialParams p) {
   // pass from the wave that computed them to the others through LDS.
   // oacc[4 * r + fs]: row block (w + r) mod 4 (r = 0 is the wave's own),
   // feature block 4 w + fs; r and fs are compile-time indices.
+  // A P tile's two 16-byte halves per lane sit in separate 1 KiB halves of
+  // the wave's 2 KiB slot, lane-contiguous, so that 16 lanes of a 16-byte
+  // LDS access hit 16 distinct bank quads.
   auto fs_write_p = [&](const PTile& pt) {
-    LDS_AS i32x4_t* dst = (LDS_AS i32x4_t*)(pbuf + wave * 2048 + lane * 32);
+    LDS_AS i32x4_t* dst = (LDS_AS i32x4_t*)(pbuf + wave * 2048 + lane * 16);
     dst[0] = i32x4_t{pt.pb[0], pt.pb[1], pt.pb[2], pt.pb[3]};
-    dst[1] = i32x4_t{pt.pb[4], pt.pb[5], pt.pb[6], pt.pb[7]};
+    dst[64] = i32x4_t{pt.pb[4], pt.pb[5], pt.pb[6], pt.pb[7]};
     scbuf[wave * 64 + lane] = pt.sc;       // lane half h: token block h's scale
   };
   auto fs_read_p = [&](int rq, i32x8_t& pb, int& sc) {
-    const LDS_AS i32x4_t* src = (const LDS_AS i32x4_t*)(pbuf + rq * 2048 + lane * 32);
-    const i32x4_t a = src[0], c = src[1];
+    const LDS_AS i32x4_t* src = (const LDS_AS i32x4_t*)(pbuf + rq * 2048 + lane * 16);
+    const i32x4_t a = src[0], c = src[64];
     pb = i32x8_t{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
     sc = scbuf[rq * 64 + lane];
   };
@@ -1606,9 +1609,9 @@ mla_partial_kernel(const PartialParams p) {
       if constexpr (FS) {
         // Publish this row block's residual tile; every wave then applies
         // all four to its feature quarter.
-        LDS_AS i32x4_t* dst = (LDS_AS i32x4_t*)(pbuf + wave * 2048 + lane * 32);
+        LDS_AS i32x4_t* dst = (LDS_AS i32x4_t*)(pbuf + wave * 2048 + lane * 16);
         dst[0] = i32x4_t{pt.pbl[0], pt.pbl[1], pt.pbl[2], pt.pbl[3]};
-        dst[1] = i32x4_t{pt.pbl[4], pt.pbl[5], pt.pbl[6], pt.pbl[7]};
+        dst[64] = i32x4_t{pt.pbl[4], pt.pbl[5], pt.pbl[6], pt.pbl[7]};
         scbuf[wave * 64 + lane] = pt.scl;
         wait_lgkm0();
         lds_barrier();
