@@ -288,7 +288,8 @@ mla_status_t mla_decode_fp8_noalloc(const void* q_nope, const void* q_pe, const 
  * The expanded keys and values are rounded to bf16 (the model's activation
  * type; the pages leave it open), products accumulate in fp32, and the
  * softmax weights enter the value product as bf16.
- * q_len is 1 .. MLA_MHA_MAX_Q_LEN.  Rows that see no token get 0 and -inf.
+ * q_len is 1 .. MLA_MHA_MAX_Q_LEN; softmax_scale must be positive and finite.
+ * Rows that see no token get 0 and -inf.
  * Two kernels on `stream` (expansion, then attention); no allocation.
  */
 size_t mla_dense_mha_workspace_size(int batch, int num_heads, int max_seq_len);

@@ -49,7 +49,7 @@ mla_status_t mla_dense_mha(const void* q_nope, const void* q_pe, const void* kv_
   if (num_blocks < 0 || max_blocks_per_seq < 1 || (int64_t)num_blocks * MLA_BLOCK_SIZE > INT32_MAX)
     return MLA_ERR_INVALID_ARGUMENT;
   if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARGUMENT;
   if (batch == 0) return MLA_OK;
   if (!q_nope || !q_pe || !block_table || !seq_lens || !w_uk || !w_uv || !out || (num_blocks > 0 && !kv_cache))
     return MLA_ERR_INVALID_ARGUMENT;

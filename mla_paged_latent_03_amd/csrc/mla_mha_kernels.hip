@@ -345,29 +345,32 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
         }
 
       // Register i of block kb holds key j0 + 32 kb + 8 (i / 4) + 4 hh + i % 4.
-      const bool masked = j0 + AT_KT > nv_min;
+      // The row maximum is taken on the raw scores (the scale is positive),
+      // and the scale and shift enter each exponent in one fma.
+      if (j0 + AT_KT > nv_min) {   // some key of the tile is past some query's causal limit
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+          for (int i = 0; i < 16; i++)
+            if (j0 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= n_vis) s[kb][i] = -INFINITY;
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          float x = s[kb][i] * c_qk;
-          if (masked && j0 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4) >= n_vis) x = -INFINITY;
-          s[kb][i] = x;
-          tmax = fmaxf(tmax, x);
-        }
+        for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(s[kb][i], s[kb][i + 1]));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m, tmax);
+      const float m_new = fmaxf(m, tmax == -INFINITY ? -INFINITY : tmax * c_qk);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-      const float sh = m_new == -INFINITY ? 0.f : m_new;
+      const float nsh = m_new == -INFINITY ? 0.f : -m_new;
       bf16x8_t pb[2][2];
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const bf16x2_t pr = {(__bf16)__builtin_amdgcn_exp2f(s[kb][i] - sh),
-                               (__bf16)__builtin_amdgcn_exp2f(s[kb][i + 1] - sh)};
+          const bf16x2_t pr = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][i], c_qk, nsh)),
+                               (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c_qk, nsh))};
           ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
           pb[kb][i / 8][i % 8] = pr[0];
           pb[kb][i / 8][i % 8 + 1] = pr[1];

@@ -307,6 +307,8 @@ def _call_mha(lib, **kw):
     (dict(odt=3), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(MB=0), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("inf")), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-0.07), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(wsb=2 * 2 * 16 * 384 * 128 * 2 - 1), binding.MLA_ERR_WORKSPACE_TOO_SMALL),
     (dict(B=65535, H=1024, msl=1 << 24, wsb=1 << 62), binding.MLA_ERR_UNSUPPORTED),
     (dict(ws=None), binding.MLA_ERR_INVALID_ARGUMENT),
