@@ -112,10 +112,10 @@ def mha_paged(q_nope, q_pe, kv_cache, block_table, seq_lens, w_uk, w_uv, scale, 
             if not keep:
                 continue
             n = max(0, L - T + t + 1)
-            o, lse = mha_decode(q_nope[b, t], q_pe[b, t], toks[:, :512], toks[:, 512:], w_uk, w_uv, scale,
-                                list(range(n)), expanded)
-            for h in keep:
-                outs[(b * T + t) * H + h] = o[h]
-                lses[(b * T + t) * H + h] = lse[h]
+            o, lse = mha_decode(q_nope[b, t][keep], q_pe[b, t][keep], toks[:, :512], toks[:, 512:], w_uk[keep],
+                                w_uv[keep], scale, list(range(n)), expanded)
+            for k, h in enumerate(keep):
+                outs[(b * T + t) * H + h] = o[k]
+                lses[(b * T + t) * H + h] = lse[k]
     order = sorted(outs) if rows is None else [int(r) for r in rows]
     return np.stack([outs[r] for r in order]), np.array([lses[r] for r in order])

@@ -145,3 +145,16 @@ def test_dense_mha_argument_errors():
         binding.mla_dense_mha(q, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, w_uk, w_uv, 10,
                               inp.softmax_scale, out, None, small)
     assert ei.value.status == binding.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_dense_mha_bench_size_sampled_rows():
+    """The benchmark's shape (4 sequences of 2048 tokens, q_len = 2048, 128
+    heads): the first and last rows of each sequence and 48 random ones."""
+    inp = wl.make_inputs(4, 128, 2048, [2048] * 4, kv_dtype="bf16", out_dtype="bf16", seed=216)
+    q, w_uk, w_uv = wl.mha_inputs(inp, seed=316)
+    n = inp.B * inp.T * inp.H
+    per_seq = inp.T * inp.H
+    edges = np.concatenate([np.arange(b * per_seq, b * per_seq + 4) for b in range(4)] +
+                           [np.arange((b + 1) * per_seq - 4, (b + 1) * per_seq) for b in range(4)])
+    rows = np.unique(np.concatenate([edges, sample_rows(n, 48, seed=216)]))
+    check(inp, q, w_uk, w_uv, "bench size", rows=rows, out_dtype="bf16")
