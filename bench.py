@@ -245,6 +245,152 @@ def mha_vs_mqa(args):
     print(json.dumps(res), flush=True)
 
 
+def _smi():
+    """(amdsmi module, handle of GPU 0), or None when the library cannot
+    reach the device."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        return amdsmi, amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:   # library missing or no device
+        log("[bench] amdsmi unavailable: %s" % e)
+        return None
+
+
+def sustain(args):
+    """Socket power, GFX clock and power-limit residency under a sustained
+    load: the workload's whole decode call back to back (rotating input sets
+    as the timed benchmark does), the streaming-read reference over the same
+    KV bytes, or nothing (idle).  Prints one JSON line."""
+    import threading
+    import torch
+    from mla_paged_latent_03_amd import binding, workloads as wl
+
+    smi = _smi()
+    if smi is None:
+        raise SystemExit("--sustain needs amdsmi and a GPU")
+    amdsmi, h = smi
+    binding.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    run = None
+    bytes_per_call = flops_per_call = 0
+    if args.sustain_kind in ("decode", "stream"):
+        log("[bench] drawing %s on %s" % (args.workload, dev))
+        inp = wl.workload(args.workload, device=dev)
+    if args.sustain_kind == "decode":
+        fp8 = inp.kv_dtype == "fp8"
+        S = binding.num_kv_splits(inp.B, inp.T, inp.H, inp.max_seq_len, inp.K, fp8)
+        out = torch.empty((inp.B, inp.T, inp.H, 512), device=dev,
+                          dtype=torch.float32 if inp.out_dtype == "f32" else torch.bfloat16)
+        lse = torch.empty((inp.B, inp.T, inp.H), device=dev, dtype=torch.float32)
+        ws_bytes = binding.workspace_size(inp.B, inp.T, inp.H, inp.max_seq_len, inp.K, fp8, S)
+        ws = torch.empty(max(1, (ws_bytes + 3) // 4), device=dev, dtype=torch.float32) if ws_bytes else None
+        sets = [inp]
+        if algorithmic_cost(inp)["total_bytes"] < (512 << 20):
+            seed0 = wl.WORKLOADS[args.workload]["seed"]
+            sets += [wl.workload(args.workload, device=dev, seed=seed0 + 100 * k) for k in (1, 2)]
+        calls = [binding.prepare_decode(x, S, out, lse, ws, stream) for x in sets]
+        cost = algorithmic_cost(inp)
+        bytes_per_call, flops_per_call = cost["total_bytes"], cost["flops"]
+
+        def run(k):
+            calls[k % len(calls)]()
+    elif args.sustain_kind == "stream":
+        ref_lib = stream_reference_lib()
+        if ref_lib is None:
+            raise SystemExit("the streaming reference library is not built")
+        nbytes = (inp.kv_cache.numel() * inp.kv_cache.element_size() // 36864) * 36864
+        sink = torch.empty(256, dtype=torch.int32, device=dev)
+        bytes_per_call = nbytes
+
+        def run(k):
+            rc = ref_lib.mla_stream_read_reference(ctypes.c_void_p(inp.kv_cache.data_ptr()), nbytes, 256,
+                                                   ctypes.c_void_p(sink.data_ptr()),
+                                                   ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError("stream reference failed (%d)" % rc)
+
+    def metrics():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        e = amdsmi.amdsmi_get_energy_count(h)
+        return m, e["energy_accumulator"] * e["counter_resolution"] * 1e-6   # J
+
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, int)]
+            samples.append((m.get("current_socket_power"), float(np.mean(clks)) if clks else None))
+            stop.wait(0.1)
+
+    if run is not None:   # a short burst first, so that the sampled window is the sustained state
+        t_end = time.perf_counter() + 0.5
+        k = 0
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                run(k)
+                k += 1
+            torch.cuda.synchronize()
+    m0, j0 = metrics()
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    next_note = t0 + 1.0
+    while time.perf_counter() - t0 < args.sustain:
+        if run is None:
+            time.sleep(0.05)
+        else:
+            for _ in range(16):
+                run(n)
+                n += 1
+            torch.cuda.synchronize()
+        if time.perf_counter() >= next_note:
+            log("[bench] sustain %s: %.0f s, %d calls" % (args.sustain_kind, time.perf_counter() - t0, n))
+            next_note += 1.0
+    dt = time.perf_counter() - t0
+    m1, j1 = metrics()
+    stop.set()
+    th.join()
+    d_acc = m1["accumulation_counter"] - m0["accumulation_counter"]
+
+    def residency(key):
+        try:
+            return round((m1[key] - m0[key]) / d_acc, 4) if d_acc else None
+        except TypeError:   # counter not reported ("N/A")
+            return None
+
+    pw = np.array([s[0] for s in samples if isinstance(s[0], (int, float))], dtype=float)
+    ck = np.array([s[1] for s in samples if s[1] is not None], dtype=float)
+
+    def stats(x):
+        return ({"median": round(float(np.median(x)), 1), "p10": round(float(np.percentile(x, 10)), 1),
+                 "p90": round(float(np.percentile(x, 90)), 1)} if x.size else None)
+
+    try:
+        cap = amdsmi.amdsmi_get_power_cap_info(h)
+    except Exception:
+        cap = {}
+    res = {"mode": "sustain", "kind": args.sustain_kind,
+           "workload": args.workload if run is not None else None,
+           "seconds": round(dt, 2), "calls": n,
+           "us_per_call": round(dt / n * 1e6, 2) if n else None,
+           "socket_power_W": stats(pw), "gfx_clock_MHz": stats(ck), "samples": int(pw.size),
+           "energy_J": round(j1 - j0, 2), "mean_power_W": round((j1 - j0) / dt, 1),
+           "energy_per_call_mJ": round((j1 - j0) / n * 1e3, 3) if n else None,
+           "ppt_residency": residency("ppt_residency_acc"),
+           "socket_thermal_residency": residency("socket_thm_residency_acc"),
+           "hbm_thermal_residency": residency("hbm_thm_residency_acc"),
+           "power_cap_W": (cap.get("power_cap") / 1e6 if isinstance(cap.get("power_cap"), (int, float)) else None),
+           "achieved_TBps": round(bytes_per_call * n / dt / 1e12, 3) if n else None,
+           "achieved_TFLOPs": round(flops_per_call * n / dt / 1e12, 1) if n and flops_per_call else None,
+           "source_hash": source_hash()}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,6 +413,12 @@ def main():
     ap.add_argument("--copy-calibration-gib", type=int, default=0,
                     help="first copy a buffer of this many GiB three times, so that a counter run over the "
                          "benchmark also reads the counters for a plain copy of known size")
+    ap.add_argument("--sustain", type=float, default=0.0,
+                    help="instead of the timed benchmark: run the load back to back for this many seconds and "
+                         "report socket power, GFX clock and power-limit residency (amdsmi)")
+    ap.add_argument("--sustain-kind", choices=("decode", "stream", "idle"), default="decode",
+                    help="load of --sustain: the workload's decode call, the streaming-read reference over its "
+                         "KV bytes, or none")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -276,6 +428,9 @@ def main():
 
     if args.mha_vs_mqa:
         mha_vs_mqa(args)
+        return
+    if args.sustain > 0:
+        sustain(args)
         return
     if args.single_launch:
         os.environ["MLA_SINGLE_LAUNCH"] = "1"
