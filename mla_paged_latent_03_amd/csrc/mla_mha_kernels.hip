@@ -54,8 +54,8 @@ __device__ __attribute__((aligned(16))) uint8_t g_mha_zero16[16];
 
 // LDS DMA: lane i copies 16 bytes from gsrc_i to LDS bytes [m0 + 16 i,
 // m0 + 16 i + 16).  Issued from inline asm, so the compiler neither waits
-// for it nor counts it; the kernel waits with vmcnt(0) before the barrier
-// that publishes the tile.  The s_nop gives the one wait state an LDS DMA
+// for it nor counts it; the kernels wait on the vector-memory counter
+// themselves before the barrier that publishes a tile.  The s_nop gives the one wait state an LDS DMA
 // needs after the SALU write of M0 that precedes it (the compiler adds none
 // before inline asm); the build scans the compiled kernels for it.
 __device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
@@ -63,6 +63,8 @@ __device__ inline void dma16(const void* gsrc, uint32_t lds_byte_addr) {
 }
 
 __device__ inline void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ inline void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 __device__ inline f32x16_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -211,8 +213,12 @@ __global__ void __launch_bounds__(256, 2) mha_expand_kernel(const MhaParams p) {
 // Attention.  Work id = (b * H + h) * chunks + (chunks - 1 - chunk): the
 // blocks of one (sequence, head) run together on one XCD, the longest
 // (last) query chunk first.  Wave w takes queries q0 + 32 w + (lane % 32).
-// Two tile buffers in LDS: while the waves compute on one, the next tile
-// streams into the other by LDS DMA, one barrier per tile.  A buffer holds
+// Two tile buffers in LDS.  A tile's K rows and its V^T rows are refilled
+// separately: the K part of tile kt+2 goes out as soon as every wave is done
+// with tile kt's QK products (second barrier of the step), the V^T part of
+// tile kt+1 as soon as every wave is done with tile kt-1's PV products
+// (first barrier), so each part has about one and a half steps to land
+// instead of one.  A buffer holds
 // the tile's K_nope rows (64 x 256 B), rope rows (64 x 128 B) and V^T rows
 // (128 x 128 B), unpadded, their 16-byte pieces XOR-swizzled (swz16 for the
 // 16-piece rows, swz8 for the 8-piece ones) so that the 16 lanes of a
@@ -301,20 +307,29 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
     }
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)tbuf;
-  int pg = n_kt > 0 ? bt[0] : -1;   // page of the next tile to fetch
-  auto fetch = [&](int j0, int buf) {
-    const int pgu = __builtin_amdgcn_readfirstlane(pg);
-    const bool pg_ok = pgu >= 0 && pgu < p.NB;
+  // The block table is read with scalar loads (uniform index), so that the
+  // only vector-memory instructions in flight in the loop are the DMAs and
+  // the waits below can count them.
+  const __attribute__((address_space(4))) int32_t* btc = (const __attribute__((address_space(4))) int32_t*)bt;
+  int pg = n_kt > 0 ? btc[0] : -1;   // page of the next tile whose keys are fetched
+  // K part of a tile (6 DMA instructions per wave: K_nope, rope).
+  auto fetch_k = [&](int j0, int buf) {
+    const bool pg_ok = pg >= 0 && pg < p.NB;
     const uint32_t lb = lds0 + (uint32_t)(buf * AT_BUF * 2);
 #pragma unroll
-    for (int i = 0; i < 10; i++) {
+    for (int i = 0; i < 6; i++) {
       const void* src;
       if (i < 4) src = ks_base + (int64_t)j0 * 128 + src_off[i];
-      else if (i < 6) src = pg_ok ? (const void*)(p.kv + (int64_t)pgu * 64 * 576 + src_off[i]) : (const void*)g_mha_zero16;
-      else src = vt_base + j0 + src_off[i];
+      else src = pg_ok ? (const void*)(p.kv + (int64_t)pg * 64 * 576 + src_off[i]) : (const void*)g_mha_zero16;
       dma16(src, lb + dst[i]);
     }
-    pg = j0 + AT_KT < n_blk ? bt[(j0 + AT_KT) >> 6] : -1;
+    pg = j0 + AT_KT < n_blk ? btc[(j0 + AT_KT) >> 6] : -1;
+  };
+  // V part of a tile (4 DMA instructions per wave).
+  auto fetch_v = [&](int j0, int buf) {
+    const uint32_t lb = lds0 + (uint32_t)(buf * AT_BUF * 2);
+#pragma unroll
+    for (int i = 6; i < 10; i++) dma16(vt_base + j0 + src_off[i], lb + dst[i]);
   };
 
   const float c_qk = p.qk_scale;   // softmax scale * log2(e)
@@ -323,15 +338,21 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
   f32x16_t o[4] = {f32x16_t{}, f32x16_t{}, f32x16_t{}, f32x16_t{}};   // O^T, dims 32 f .. 32 f + 31
   const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
 
-  if (n_kt > 0) fetch(0, 0);
-  if (n_kt > 1) fetch(AT_KT, 1);
-  wait_vmcnt0();
-  __syncthreads();
+  // Per wave, DMAs go out in the order K(0) V(0) K(1), then in tile kt
+  // V(kt+1) after the first barrier and K(kt+2) after the second, so that
+  // K(kt) is followed by V(kt) and K(kt+1), and V(kt) by K(kt+1) and V(kt+1).
+  if (n_kt > 0) { fetch_k(0, 0); fetch_v(0, 0); }
+  if (n_kt > 1) fetch_k(AT_KT, 1);
   for (int kt = 0; kt < n_kt; kt++) {
     const int j0 = kt * AT_KT;
+    if (kt + 1 < n_kt) wait_vmcnt<10>();
+    else wait_vmcnt<4>();
+    __syncthreads();   // K(kt) in LDS; every wave is done with tile kt-1's V^T
+    if (kt + 1 < n_kt) fetch_v(j0 + AT_KT, (kt + 1) & 1);
     const __bf16* kn_l = tbuf + (kt & 1) * AT_BUF;   // K_nope rows
     const __bf16* kr_l = kn_l + AT_NOPE;               // rope rows
     const __bf16* vb_l = kr_l + AT_ROPE;               // V^T rows
+    bf16x8_t pb[2][2];   // this tile's weights (P^T operand)
     if (j0 < nv_max) {   // some query of this wave sees the tile
       f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
@@ -363,7 +384,6 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
       const float m_new = fmaxf(m, tmax == -INFINITY ? -INFINITY : tmax * c_qk);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
       const float nsh = m_new == -INFINITY ? 0.f : -m_new;
-      bf16x8_t pb[2][2];
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
@@ -383,6 +403,12 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
 #pragma unroll
           for (int i = 0; i < 16; i++) o[f][i] *= alpha;
       }
+    }
+    if (kt + 1 < n_kt) wait_vmcnt<10>();
+    else wait_vmcnt0();
+    __syncthreads();   // V(kt) in LDS; every wave is done with tile kt's K rows
+    if (kt + 2 < n_kt) fetch_k(j0 + 2 * AT_KT, kt & 1);
+    if (j0 < nv_max) {
       // V^T on the A side: row = dim 32 f + l32, keys 16 s + [8 hh, 8 hh + 8)
       // in stored order, which is the order of P's group s (block s / 2,
       // registers 8 (s % 2) ..).
@@ -394,9 +420,6 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
           o[f] = mfma16(lds8(vb_l + (d * 8 + swz8(d, 2 * s4 + hh)) * 8), pb[s4 >> 1][s4 & 1], o[f]);
         }
     }
-    wait_vmcnt0();     // this wave's DMAs of tile kt + 1 have landed
-    __syncthreads();   // tile kt + 1 complete; every wave is done with tile kt's buffer
-    if (kt + 2 < n_kt) fetch(j0 + 2 * AT_KT, kt & 1);
   }
 
   const float l_tot = l + __shfl_xor(l, 32);
