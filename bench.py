@@ -296,6 +296,18 @@ def sustain(args):
 
         def run(k):
             calls[k % len(calls)]()
+    elif args.sustain_kind == "mha":
+        B, L, H = args.mha_batch, args.mha_len, args.mha_heads
+        inp = wl.make_inputs(B, H, L, [L] * B, kv_dtype="bf16", out_dtype="bf16", seed=1101, device=dev)
+        q, w_uk, w_uv = wl.mha_inputs(inp, seed=1102, device=dev)
+        out = torch.empty((B, L, H, 128), device=dev, dtype=torch.bfloat16)
+        lse = torch.empty((B, L, H), device=dev, dtype=torch.float32)
+        ws = torch.empty((binding.dense_mha_workspace_size(B, H, L) + 1) // 2, device=dev, dtype=torch.bfloat16)
+        flops_per_call = 2 * 256 * 512 * B * L * H + 2 * (192 + 128) * H * B * L * (L + 1) // 2
+
+        def run(k):
+            binding.mla_dense_mha(q, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens, w_uk, w_uv, L,
+                                  inp.softmax_scale, out, lse, ws, stream)
     elif args.sustain_kind == "stream":
         ref_lib = stream_reference_lib()
         if ref_lib is None:
@@ -375,7 +387,8 @@ def sustain(args):
     except Exception:
         cap = {}
     res = {"mode": "sustain", "kind": args.sustain_kind,
-           "workload": args.workload if run is not None else None,
+           "workload": ("prefill_b%d_h%d_len%d_bf16" % (args.mha_batch, args.mha_heads, args.mha_len)
+                        if args.sustain_kind == "mha" else args.workload if run is not None else None),
            "seconds": round(dt, 2), "calls": n,
            "us_per_call": round(dt / n * 1e6, 2) if n else None,
            "socket_power_W": stats(pw), "gfx_clock_MHz": stats(ck), "samples": int(pw.size),
@@ -385,7 +398,7 @@ def sustain(args):
            "socket_thermal_residency": residency("socket_thm_residency_acc"),
            "hbm_thermal_residency": residency("hbm_thm_residency_acc"),
            "power_cap_W": (cap.get("power_cap") / 1e6 if isinstance(cap.get("power_cap"), (int, float)) else None),
-           "achieved_TBps": round(bytes_per_call * n / dt / 1e12, 3) if n else None,
+           "achieved_TBps": round(bytes_per_call * n / dt / 1e12, 3) if n and bytes_per_call else None,
            "achieved_TFLOPs": round(flops_per_call * n / dt / 1e12, 1) if n and flops_per_call else None,
            "source_hash": source_hash()}
     print(json.dumps(res), flush=True)
@@ -416,9 +429,9 @@ def main():
     ap.add_argument("--sustain", type=float, default=0.0,
                     help="instead of the timed benchmark: run the load back to back for this many seconds and "
                          "report socket power, GFX clock and power-limit residency (amdsmi)")
-    ap.add_argument("--sustain-kind", choices=("decode", "stream", "idle"), default="decode",
+    ap.add_argument("--sustain-kind", choices=("decode", "stream", "mha", "idle"), default="decode",
                     help="load of --sustain: the workload's decode call, the streaming-read reference over its "
-                         "KV bytes, or none")
+                         "KV bytes, the dense MHA call of --mha-vs-mqa, or none")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
