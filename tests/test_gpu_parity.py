@@ -447,6 +447,24 @@ def test_sparse_fp8_shapes(H, T, lens, K, splits):
     check_full(inp, splits, "sparse fp8 H=%d K=%d" % (H, K))
 
 
+@pytest.mark.parametrize("kv_dtype,H,T,lens,K,splits", [
+    ("bf16", 256, 1, [3000, 700], 512, 0),       # two head blocks of 128 rows
+    ("fp8", 160, 2, [2000, 600], 256, 0),        # MTP; the second head block holds 32 real rows
+    ("bf16", 40, 3, [900, 2500], 192, 0),        # a head count that is not a multiple of 32
+    ("fp8", 1024, 1, [1500, 300], 128, 2),       # eight head blocks, two splits
+    ("bf16", 80, 4, [5000, 40, 1200], 320, 1),   # one split, a sequence shorter than K
+])
+def test_sparse_heads_over_several_row_blocks(kv_dtype, H, T, lens, K, splits):
+    """Sparse calls whose heads span several row blocks, or whose last block
+    is partly padding: every block of a draft token reads that token's index
+    list, and padding rows are neither read nor written."""
+    inp = wl.make_inputs(len(lens), H, T, lens, kv_dtype=kv_dtype, out_dtype="f32", topk=K, seed=61 + H + T,
+                         poison=True)
+    waves = binding.launch_waves(inp.B, inp.T, inp.H, inp.max_len, K, kv_dtype == "fp8")
+    assert H > 32 * waves or H % 32 != 0
+    check_full(inp, splits, "sparse heads H=%d T=%d %s" % (H, T, kv_dtype))
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 def test_sparse_out_of_range_and_duplicate_indices(kv_dtype):
     inp = wl.make_inputs(2, 16, 1, [300, 300], kv_dtype=kv_dtype, out_dtype="f32", topk=128, seed=14)
