@@ -79,6 +79,8 @@ def test_tiny_workload_split_results_agree():
     (32, 8, [9, 640, 1111], 3),               # 256 rows: two row blocks
     (128, 8, [100, 900], 0),                  # 1024 rows: eight row blocks
     (24, 3, [50, 513], 0),                    # rows not a multiple of 32
+    (40, 8, [90, 2100], 0),                   # 320 rows: the third four-wave block half empty
+    (40, 8, [90, 2100], 2),
 ])
 def test_dense_bf16_shapes(H, T, lens, splits):
     inp = wl.make_inputs(len(lens), H, T, lens, kv_dtype="bf16", out_dtype="f32", seed=7 + H + T, poison=True,
@@ -165,6 +167,8 @@ def test_scale_is_read_every_call():
     (32, 4, [4, 100, 300, 700], 3),
     (16, 1, [1, 64, 129], 2),
     (128, 2, [257, 1000], 0),
+    (48, 5, [300, 3000], 0),                  # 240 rows: the second four-wave block partly empty
+    (48, 5, [300, 3000], 3),
 ])
 def test_dense_fp8_shapes(H, T, lens, splits):
     inp = wl.make_inputs(len(lens), H, T, lens, kv_dtype="fp8", out_dtype="f32", seed=11 + H, poison=True,
