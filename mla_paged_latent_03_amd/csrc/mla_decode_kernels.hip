@@ -1525,6 +1525,22 @@ mla_partial_kernel(const PartialParams p) {
       // iteration from a page read early in it, off the iteration's start.
       DmaSrc src = dma_prepare(1);
       int pg_nx = 0;
+      // A wave whose rows are all past the block's end (the second wave of a
+      // two-wave block over at most 32 rows) only moves its share of each
+      // tile: its products would be discarded, and they cost power.
+      // (A separate loop: a branch inside the computing loop makes the
+      // compiler spill the accumulators around it.)
+      const bool wave_busy = __builtin_amdgcn_ballot_w64(row_ok) != 0;
+      if (RG > 1 && !wave_busy) {
+        for (int i = 0; i < n_tiles; i++) {
+          wait_vmcnt<0>();
+          lds_barrier();   // the same barriers as the computing waves
+#pragma unroll
+          for (int j = 0; j < NI; j++) dma_issue(src, (i + 1) % NS, j);
+          pg_nx = dma_page(i + 2);
+          src = dma_prepare_pg(i + 2, pg_nx);
+        }
+      } else
       for (int i = 0; i < n_tiles; i++) {
         wait_vmcnt<0>();
         if (RG > 1) lds_barrier();   // tile i complete; every wave is done with tile i-1's slot
