@@ -261,7 +261,8 @@ def sustain(args):
     """Socket power, GFX clock and power-limit residency under a sustained
     load: the workload's whole decode call back to back (rotating input sets
     as the timed benchmark does), the streaming-read reference over the same
-    KV bytes, or nothing (idle).  Prints one JSON line."""
+    KV bytes, the dense MHA call of --mha-vs-mqa, or nothing (idle).  Prints
+    one JSON line."""
     import threading
     import torch
     from mla_paged_latent_03_amd import binding, workloads as wl
