@@ -382,3 +382,17 @@ def test_bf16_expanded_mha_rounds_the_expanded_keys_and_values():
     assert np.abs(o_u - o_b).max() > 1e-6          # the rounding is not a no-op
     o_e, l_e = mb.mha_paged(q_nope, q_pe, kv_r, bt, np.array(lens), w_uk, w_uv, scale, expanded="bf16")
     assert np.array_equal(o_e, o_f) and np.array_equal(l_e, l_f)
+
+
+def test_parity_bound_half_ulp_of_bf16():
+    """The parity bound for bf16 outputs adds half a bf16 ulp of the value:
+    exact at powers of two, and never exceeded by torch's round-to-nearest
+    fp32 -> bf16 conversion."""
+    from parity import half_ulp_bf16
+    assert list(half_ulp_bf16(np.array([0.0, 1.0, 1.99, 2.0, -4.0, 7.9, 0.25]))) == \
+        [0.0, 2.0 ** -8, 2.0 ** -8, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -10]
+    x = np.random.default_rng(5).normal(0.0, 3.0, 100000).astype(np.float32)
+    r = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    d = np.abs(r.astype(np.float64) - x)
+    assert np.all(d <= half_ulp_bf16(np.maximum(np.abs(x), np.abs(r))))
+    assert np.any(d > 0.99 * half_ulp_bf16(np.abs(x)))   # and it is tight: some roundings reach it
