@@ -162,3 +162,38 @@ def test_dense_mha_bench_size_sampled_rows():
                            [np.arange((b + 1) * per_seq - 4, (b + 1) * per_seq) for b in range(4)])
     rows = np.unique(np.concatenate([edges, sample_rows(n, 48, seed=216)]))
     check(inp, q, w_uk, w_uv, "bench size", rows=rows, out_dtype="bf16")
+
+
+# A seeded random sweep of shapes: batch, heads, lengths (empty, one-token and
+# page-edge ones among them), q_len from a decode step to a whole prefill, and
+# the output dtype, drawn together.  Rows beyond a few hundred are sampled
+# (first and last rows included), since the oracle expands each row's keys.
+def _draw_mha_cases(n=12, seed=20261204):
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(g.integers(1, 5))
+        H = int(g.choice([1, 2, 3, 8, 16, 33]))
+        lens = [int(g.choice([0, 1, 127, 128, 129])) if g.random() < 0.3 else int(g.integers(1, 701))
+                for _ in range(B)]
+        if max(lens) == 0:
+            lens[0] = 1
+        T = [1, int(g.integers(2, 17)), max(lens)][i % 3]
+        out_dtype = "f32" if g.random() < 0.5 else "bf16"
+        cases.append(dict(B=B, H=H, T=T, lens=lens, out_dtype=out_dtype, seed=900 + i))
+    return cases
+
+
+MHA_CASES = _draw_mha_cases()
+
+
+@pytest.mark.parametrize("case", MHA_CASES,
+                         ids=["B%d-T%d-H%d-%s" % (c["B"], c["T"], c["H"], c["out_dtype"]) for c in MHA_CASES])
+def test_dense_mha_random_shapes(case):
+    inp = wl.make_inputs(case["B"], case["H"], case["T"], case["lens"], kv_dtype="bf16", out_dtype=case["out_dtype"],
+                         seed=case["seed"], poison=True, extra_pages=1)
+    q, w_uk, w_uv = wl.mha_inputs(inp, seed=case["seed"] + 50)
+    n = inp.B * inp.T * inp.H
+    rows = None if n <= 256 else np.unique(np.concatenate([sample_rows(n, 64, seed=case["seed"]),
+                                                            np.arange(min(8, n)), np.arange(n - min(8, n), n)]))
+    check(inp, q, w_uk, w_uv, "random lens=%s" % case["lens"], rows=rows, out_dtype=case["out_dtype"])
