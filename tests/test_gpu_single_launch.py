@@ -128,3 +128,46 @@ def test_graph_replay_and_calls_in_between():
     compare(so, sl, ref_o, ref_l, "fp8", what="call between replays")
     ref_o, ref_l = oracle_rows(inp.to("cpu"))
     compare(eager_o, eager_l, ref_o, ref_l, "fp8", what="captured call")
+
+
+# A seeded random sweep of small shapes with the single-launch form
+# requested (the library plans it where every unit is resident at once and
+# falls back to two launches elsewhere), every row against the oracle.
+def _random_cases(n=30, seed=20261206):
+    import test_gpu_random_shapes as rs
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kind = ["bf16", "fp8", "sparse_bf16", "sparse_fp8"][i % 4]
+        sparse = kind.startswith("sparse")
+        B, T = int(g.integers(1, 7)), int(g.integers(1, 9))
+        H = int(g.choice([1, 5, 16, 32, 40, 64, 128]))
+        K = int(g.choice([32, 96, 200, 512])) if sparse else 0
+        l_max = 8 * K + 100 if sparse else min(4000, max(8, rs.PAIR_CAP // (B * T * H)))
+        lens = [int(g.choice(rs.SPECIAL_LENS)) if g.random() < 0.3 else int(g.integers(1, l_max + 1))
+                for _ in range(B)]
+        if max(lens) == 0:
+            lens[0] = 1
+        if sparse and B * T * H * K > rs.PAIR_CAP:
+            H = max(1, rs.PAIR_CAP // (B * T * K))
+        cases.append(dict(kind=kind, B=B, T=T, H=H, K=K, lens=lens, splits=int(g.choice([0, 2, 3, 5])),
+                          seed=1200 + i))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=["%s-B%d-T%d-H%d-K%d-S%d" % (c["kind"], c["B"], c["T"], c["H"], c["K"],
+                                                                          c["splits"]) for c in RANDOM])
+def test_single_launch_random_shapes(case):
+    kv_dtype = "fp8" if case["kind"].endswith("fp8") else "bf16"
+    inp = wl.make_inputs(case["B"], case["H"], case["T"], case["lens"], kv_dtype=kv_dtype, out_dtype="f32",
+                         topk=case["K"] or None, seed=case["seed"], poison=True)
+    what = "single launch random %s lens=%s" % (case["kind"], case["lens"])
+    _say("[gpu] %s" % what)
+    with single_launch():
+        out, lse, _ = binding.decode(inp.to(DEV), num_kv_splits=case["splits"])
+        torch.cuda.synchronize()
+    ref_o, ref_l = oracle_rows(inp)
+    compare(out, lse, ref_o, ref_l, kv_dtype, what=what)
