@@ -80,8 +80,9 @@
  *    representable (the same review flags an unsafe fallback for them).
  *  - Errors the host can see are returned BEFORE any launch, and nothing is
  *    enqueued: bad dims, T outside [1, 8], block_size != 64, a NULL required
- *    pointer, num_kv_splits outside [0, MLA_MAX_KV_SPLITS], a workspace
- *    smaller than mla_workspace_size().  A split may cover at most 1024
+ *    pointer, num_kv_splits outside [0, MLA_MAX_KV_SPLITS], a softmax_scale
+ *    (or fp8 q_scale / kv_scale) that is not positive and finite, a
+ *    workspace smaller than mla_workspace_size().  A split may cover at most 1024
  *    pages (dense) or 1024 top-k entries (sparse); an explicit num_kv_splits
  *    that violates this returns MLA_ERR_UNSUPPORTED (the library's own choice
  *    never does).  A failed launch returns MLA_ERR_HIP.

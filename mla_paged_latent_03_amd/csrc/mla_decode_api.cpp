@@ -261,8 +261,11 @@ mla_status_t run(Kind kind, const void* q_nope, const void* q_pe, const void* kv
   if (NB < 0 || MB < 1 || (int64_t)NB * MLA_BLOCK_SIZE > INT32_MAX) return MLA_ERR_INVALID_ARGUMENT;
   if (num_kv_splits < 0 || num_kv_splits > MLA_MAX_KV_SPLITS) return MLA_ERR_INVALID_ARGUMENT;
   if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_F32) return MLA_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(softmax_scale) || !std::isfinite(q_scale) || !std::isfinite(kv_scale) || q_scale <= 0.f ||
-      kv_scale <= 0.f)
+  // The kernels take each row's softmax reference from the maximum of the
+  // raw scores, which is the maximum of the scaled ones only for a positive
+  // scale (a zero scale would also turn masked scores, -inf * 0, into NaN).
+  if (!std::isfinite(softmax_scale) || !std::isfinite(q_scale) || !std::isfinite(kv_scale) || softmax_scale <= 0.f ||
+      q_scale <= 0.f || kv_scale <= 0.f)
     return MLA_ERR_INVALID_ARGUMENT;
   if (B == 0) return MLA_OK;
   const bool stage1_only = out == nullptr && lse == nullptr;

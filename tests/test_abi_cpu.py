@@ -150,6 +150,8 @@ def _call_dense(lib, **kw):
     (dict(splits=300), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(splits=-1), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("nan")), binding.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), binding.MLA_ERR_INVALID_ARGUMENT),       # the row reference needs a positive scale
+    (dict(scale=-0.07), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(MB=0), binding.MLA_ERR_INVALID_ARGUMENT),
     (dict(splits=2, ws=FAKE, wsb=2 * 16 * 2 * 513 * 4 - 1), binding.MLA_ERR_WORKSPACE_TOO_SMALL),
     (dict(splits=2, ws=None, wsb=0), binding.MLA_ERR_WORKSPACE_TOO_SMALL),
