@@ -8,7 +8,7 @@ import re
 
 import pytest
 
-from mla_paged_latent_03_amd import binding
+from mla_paged_latent_03_amd import binding, workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla_decode.h")
@@ -322,3 +322,15 @@ def test_dense_mha_argument_errors(lib, kw, status):
 
 def test_dense_mha_empty_batch_is_a_no_op(lib):
     assert _call_mha(lib, B=0, q=None, out=None, ws=None, wsb=0) == binding.MLA_OK
+
+
+def test_product_path_fails_loudly_without_the_library_or_a_gpu(monkeypatch):
+    """No CPU fallback: a missing library raises at load, and host tensors are
+    refused before anything reaches the C ABI."""
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(ImportError):
+        binding.load("/nonexistent/libmla_decode.so")
+    monkeypatch.undo()
+    inp = wl.make_inputs(1, 16, 1, [40], kv_dtype="bf16", out_dtype="f32", seed=3)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.decode(inp)
