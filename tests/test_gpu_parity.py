@@ -673,3 +673,21 @@ def test_stage_one_then_merge_equals_one_call(kv_dtype):
     binding.mla_merge_partials(ws, inp.B * inp.T * inp.H, 3, out, lse)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+
+
+# ------------------------------------------------------------------ the largest shapes the calls accept
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "sparse", "sparse_fp8"])
+def test_maximum_heads_and_draft_length(kind):
+    """H = 1024 heads with q_len = 8: 8192 rows per sequence (64 four-wave row
+    blocks, or 8 head blocks per draft token for sparse lists), next to a short
+    sequence; the first and last sequence's edge rows and a random sample."""
+    kv_dtype = "fp8" if kind.endswith("fp8") else "bf16"
+    K = 256 if kind.startswith("sparse") else None
+    inp = wl.make_inputs(2, 1024, 8, [700, 40], kv_dtype=kv_dtype, out_dtype="bf16", topk=K, seed=91, poison=True)
+    out, lse = run_case(inp, 0, "max heads %s" % kind)
+    n = inp.B * inp.T * inp.H
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(n - 64, n), sample_rows(n, 384, seed=91)]))
+    ref_o, ref_l = oracle_rows(inp, rows=rows)
+    e = compare(out, lse, ref_o, ref_l, kv_dtype, rows=rows, what="max heads %s" % kind)
+    _say("[gpu] max heads %s: max |out - oracle| %.4g, lse rel %.3g" % ((kind,) + e))
