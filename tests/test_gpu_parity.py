@@ -691,3 +691,24 @@ def test_maximum_heads_and_draft_length(kind):
     ref_o, ref_l = oracle_rows(inp, rows=rows)
     e = compare(out, lse, ref_o, ref_l, kv_dtype, rows=rows, what="max heads %s" % kind)
     _say("[gpu] max heads %s: max |out - oracle| %.4g, lse rel %.3g" % ((kind,) + e))
+
+
+@pytest.mark.parametrize("kind,T", [("bf16", 1), ("fp8", 4), ("sparse", 2), ("sparse_fp8", 1)])
+def test_every_sequence_empty(kind, T):
+    """A batch in which no sequence holds a token (max_seq_len 0): every row
+    comes out as zeros with lse -inf, in every kind."""
+    kv_dtype = "fp8" if kind.endswith("fp8") else "bf16"
+    K = 64 if kind.startswith("sparse") else None
+    inp = wl.make_inputs(3, 16, T, [0, 0, 0], kv_dtype=kv_dtype, out_dtype="f32", topk=K, seed=93, extra_pages=1)
+    out, lse = run_case(inp, 0, "all empty %s" % kind)
+    assert torch.count_nonzero(out).item() == 0
+    assert torch.isneginf(lse).all().item()
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_sparse_list_longer_than_many_splits(kv_dtype):
+    """A top-k list of 20000 indices over 30000 tokens: at least 20 splits of
+    the 1024-entry index table, every row against the oracle."""
+    inp = wl.make_inputs(1, 16, 1, [30000], kv_dtype=kv_dtype, out_dtype="f32", topk=20000, seed=94, poison=True)
+    assert binding.num_kv_splits(1, 1, 16, inp.max_len, 20000, kv_dtype == "fp8") >= 20
+    check_full(inp, 0, "sparse K=20000 %s" % kv_dtype)
