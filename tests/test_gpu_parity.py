@@ -712,3 +712,35 @@ def test_sparse_list_longer_than_many_splits(kv_dtype):
     inp = wl.make_inputs(1, 16, 1, [30000], kv_dtype=kv_dtype, out_dtype="f32", topk=20000, seed=94, poison=True)
     assert binding.num_kv_splits(1, 1, 16, inp.max_len, 20000, kv_dtype == "fp8") >= 20
     check_full(inp, 0, "sparse K=20000 %s" % kv_dtype)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_zero_query_is_the_mean_of_the_visible_latents(kv_dtype):
+    """q = 0 makes every weight equal: out is the mean of the latents a row
+    sees and lse = ln(tokens seen), over long units (a dropped or repeated
+    tile shows at once).  Checked against that closed form in fp64."""
+    lens = [50000, 7777, 1]
+    inp = wl.make_inputs(3, 16, 4, lens, kv_dtype=kv_dtype, out_dtype="f32", seed=95)
+    inp.q_nope.zero_()
+    inp.q_pe.zero_()
+    out, lse = run_case(inp, 0, "zero query %s" % kv_dtype)
+    kv = inp.kv_cache
+    if kv_dtype == "fp8":
+        lat = kv.view(torch.float8_e4m3fn).to(torch.float64)[..., :512] * inp.kv_scale
+    else:
+        lat = kv.to(torch.float64)[..., :512]
+    o = out.double().cpu()
+    for b, L in enumerate(lens):
+        pages = [int(p) for p in inp.block_table[b, :(L + 63) // 64]]
+        toks = torch.cat([lat[p] for p in pages], dim=0)[:L]
+        csum = torch.cumsum(toks, dim=0)
+        for t in range(4):
+            n = L - 4 + t + 1
+            if n <= 0:
+                assert torch.count_nonzero(o[b, t]).item() == 0 and torch.isneginf(lse[b, t]).all().item()
+                continue
+            mean = csum[n - 1] / n
+            err = float((o[b, t] - mean).abs().max())
+            assert err < 1e-4, "b=%d t=%d n=%d: max |out - mean| = %.3g" % (b, t, n, err)
+            lerr = float((lse[b, t].double().cpu() - math.log(n)).abs().max())
+            assert lerr < 1e-5 * max(1.0, math.log(n)), "b=%d t=%d: lse %.3g off" % (b, t, lerr)
