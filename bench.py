@@ -117,6 +117,47 @@ def stream_reference_lib():
     return lib
 
 
+def lds_rate(args):
+    """LDS read rate of this GPU, from the reference library's read-rate
+    kernel: bytes per shader clock for 16-byte ds_read_b128 reads, by waves
+    per workgroup and reads each lane keeps in flight, one workgroup per
+    compute unit.  Prints one JSON line."""
+    import torch
+    lib = stream_reference_lib()
+    if lib is None:
+        raise SystemExit("libmla_stream_ref.so is not built: run __graft_entry__.build() first")
+    fn = lib.mla_lds_read_rate_reference
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rows = []
+    for waves in (1, 2, 4, 8, 16):
+        for inflight in (2, 4, 8, 16):
+            iters = 64000 // inflight                      # 64000 reads per lane
+            sink = torch.empty(n_cu * 64 * waves, dtype=torch.int32, device=dev)
+            clocks = torch.zeros(2 * n_cu, dtype=torch.int64, device=dev)
+            khz = ctypes.c_int(0)
+            for _ in range(2):                             # the first launch warms up
+                rc = fn(waves, inflight, n_cu, iters, sink.data_ptr(), clocks.data_ptr(), ctypes.byref(khz), stream)
+                if rc != 0:
+                    raise SystemExit("mla_lds_read_rate_reference failed (%d)" % rc)
+            torch.cuda.synchronize()
+            c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+            cyc, ticks = float(np.median(c[:, 0])), float(np.median(c[:, 1]))
+            per_wg = 64.0 * waves * iters * inflight * 16 / cyc
+            rows.append({"waves": waves, "reads_in_flight_per_wave": inflight,
+                         "bytes_per_clk_per_workgroup": round(per_wg, 1),
+                         "bytes_per_clk_per_wave": round(per_wg / waves, 1),
+                         "clock_MHz": round(cyc / (ticks / (khz.value * 1e3)) / 1e6, 0)})
+            log("[bench] lds rate: %2d waves, %2d reads in flight: %6.1f B/clk per workgroup (%5.1f per wave)"
+                % (waves, inflight, per_wg, per_wg / waves))
+    print(json.dumps({"mode": "lds_rate", "read": "ds_read_b128, 16 B per lane, 64 KiB LDS array",
+                      "workgroups": n_cu, "rows": rows}), flush=True)
+
+
 def load_traffic(workload: str):
     """HBM bytes per launch of the partial kernel from the rocprofv3 PMC runs
     recorded for this workload, if they were taken on the current sources."""
@@ -433,6 +474,9 @@ def main():
     ap.add_argument("--sustain-kind", choices=("decode", "stream", "mha", "idle"), default="decode",
                     help="load of --sustain: the workload's decode call, the streaming-read reference over its "
                          "KV bytes, the dense MHA call of --mha-vs-mqa, or none")
+    ap.add_argument("--lds-rate", action="store_true",
+                    help="instead of the timed benchmark: measure the LDS read rate (bytes per clock) by waves "
+                         "per workgroup and reads in flight per wave")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -445,6 +489,9 @@ def main():
         return
     if args.sustain > 0:
         sustain(args)
+        return
+    if args.lds_rate:
+        lds_rate(args)
         return
     if args.single_launch:
         os.environ["MLA_SINGLE_LAUNCH"] = "1"
