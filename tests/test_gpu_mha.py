@@ -197,3 +197,52 @@ def test_dense_mha_random_shapes(case):
     rows = None if n <= 256 else np.unique(np.concatenate([sample_rows(n, 64, seed=case["seed"]),
                                                             np.arange(min(8, n)), np.arange(n - min(8, n), n)]))
     check(inp, q, w_uk, w_uv, "random lens=%s" % case["lens"], rows=rows, out_dtype=case["out_dtype"])
+
+
+def test_dense_mha_graph_replay():
+    """mla_dense_mha captured in a HIP graph: four replays, each after the
+    outputs were overwritten with NaN and with an unrelated eager MHA call in
+    between, equal the eager call bit for bit; the eager call matches the
+    oracle.  The call allocates nothing and records no memset."""
+    inp = wl.make_inputs(3, 8, 24, [24, 300, 5], kv_dtype="bf16", out_dtype="bf16", seed=214)
+    q, w_uk, w_uv = wl.mha_inputs(inp, seed=314)
+    g_in = inp.to(DEV)
+    qd, ukd, uvd = q.to(DEV), w_uk.to(DEV), w_uv.to(DEV)
+    need = binding.dense_mha_workspace_size(inp.B, inp.H, inp.max_seq_len)
+    ws = torch.empty((need + 1) // 2, device=DEV, dtype=torch.bfloat16)
+
+    def call(out, lse, stream=None):
+        binding.mla_dense_mha(qd, g_in.q_pe, g_in.kv_cache, g_in.block_table, g_in.seq_lens, ukd, uvd,
+                              g_in.max_seq_len, g_in.softmax_scale, out, lse, ws, stream=stream)
+
+    eager_o = torch.empty((inp.B, inp.T, inp.H, 128), device=DEV, dtype=torch.bfloat16)
+    eager_l = torch.empty((inp.B, inp.T, inp.H), device=DEV, dtype=torch.float32)
+    _say("[gpu] mha graph: eager call")
+    call(eager_o, eager_l)
+    torch.cuda.synchronize()
+    out, lse = torch.empty_like(eager_o), torch.empty_like(eager_l)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call(out, lse, stream=s)            # warm the stream
+        torch.cuda.synchronize()
+        _say("[gpu] mha graph: capture")
+        with torch.cuda.graph(g, stream=s):
+            call(out, lse, stream=s)
+    other_o, other_l = torch.empty_like(eager_o), torch.empty_like(eager_l)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        _say("[gpu] mha graph: replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), "replay %d differs" % rep
+        call(other_o, other_l)              # unrelated eager work between replays
+        torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mha(inp, q, w_uk, w_uv)
+    o = eager_o.double().cpu().reshape(-1, 128).numpy()
+    allowed = TOL + half_ulp_bf16(np.maximum(np.abs(ref_o), np.abs(o)))
+    assert np.all(np.abs(o - ref_o) <= allowed)
+    l = eager_l.double().cpu().reshape(-1).numpy()
+    assert np.array_equal(np.isneginf(l), np.isneginf(ref_l))
