@@ -628,6 +628,39 @@ def test_hip_graph_replay_matches_eager(lens, splits):
     compare(eager_o, eager_l, ref_o, ref_l, "fp8", what="graph replay %s" % lens)
 
 
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_hip_graph_replay_sparse_matches_eager(kv_dtype):
+    """Sparse calls (per-draft-token index lists, several splits, the merge)
+    captured in one graph: four replays with NaN-filled outputs and other
+    eager calls between them equal the eager call bit for bit."""
+    B, T, H, K = 3, 2, 40, 300
+    inp = wl.make_inputs(B, H, T, [5000, 90, 1], kv_dtype=kv_dtype, out_dtype="bf16", topk=K, seed=18).to(DEV)
+    splits = 3
+    _say("[gpu] sparse graph capture %s: K=%d, %d splits" % (kv_dtype, K, splits))
+    eager_o, eager_l, ws = binding.decode(inp, num_kv_splits=splits)
+    torch.cuda.synchronize()
+    out, lse = torch.empty_like(eager_o), torch.empty_like(eager_l)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        binding.decode(inp, num_kv_splits=splits, out=out, lse=lse, workspace=ws)   # warm the stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            binding.decode(inp, num_kv_splits=splits, out=out, lse=lse, workspace=ws, stream=s)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), "replay %d differs" % rep
+        binding.decode(inp, num_kv_splits=1)   # unrelated eager work between replays
+        torch.cuda.synchronize()
+    ref_o, ref_l = oracle_rows(inp.to("cpu"))
+    compare(eager_o, eager_l, ref_o, ref_l, kv_dtype, what="sparse graph replay %s" % kv_dtype)
+
+
 # ------------------------------------------------------------------ full-size workloads (sampled rows)
 
 FULL = ["r1_b128_h16_kv1k-8k_bf16", "mtp3_b64_h32_kv80k_fp8", "mtp7_b32_h128_kv16k-32k_bf16",
