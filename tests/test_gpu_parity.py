@@ -661,6 +661,57 @@ def test_hip_graph_replay_sparse_matches_eager(kv_dtype):
     compare(eager_o, eager_l, ref_o, ref_l, kv_dtype, what="sparse graph replay %s" % kv_dtype)
 
 
+
+def test_hip_graph_replay_two_rounds_bf16():
+    """A dense bf16 call planned as two rounds of longest-first pieces (the
+    device cuts and ranks the pieces from seq_lens inside the graph): four
+    replays equal to the eager call bit for bit; then the lengths are cut
+    down in place on the device (the captured max_seq_len bound still
+    holds) and a replay equals a fresh eager call on the new lengths."""
+    B, T, H = 32, 8, 128
+    g_len = np.random.default_rng(19)
+    lens = [int(x) for x in g_len.integers(100, 1501, size=B)]
+    assert binding.num_kv_splits(B, T, H, max(lens), 0, False) == 2
+    inp = wl.make_inputs(B, H, T, lens, kv_dtype="bf16", out_dtype="bf16", seed=19).to(DEV)
+    _say("[gpu] graph capture, two rounds longest first, B=%d H=%d T=%d" % (B, H, T))
+    eager_o, eager_l, ws = binding.decode(inp)
+    torch.cuda.synchronize()
+    out, lse = torch.empty_like(eager_o), torch.empty_like(eager_l)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        binding.decode(inp, out=out, lse=lse, workspace=ws)   # warm the stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            binding.decode(inp, out=out, lse=lse, workspace=ws, stream=s)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), "replay %d differs" % rep
+        binding.decode(inp, num_kv_splits=1)   # unrelated eager work between replays
+        torch.cuda.synchronize()
+    n = B * T * H
+    rows = np.unique(np.concatenate([np.arange(0, T * H), sample_rows(n, 256, seed=19)]))
+    ref_o, ref_l = oracle_rows(inp.to("cpu"), rows=rows)
+    compare(eager_o, eager_l, ref_o, ref_l, "bf16", rows=rows, what="graph replay two rounds bf16")
+    # New, shorter lengths written into the captured seq_lens buffer.
+    new_lens = [max(1, L - int(g_len.integers(0, L // 2 + 1))) for L in lens]
+    inp.seq_lens.copy_(torch.tensor(new_lens, dtype=inp.seq_lens.dtype))
+    torch.cuda.synchronize()
+    _say("[gpu] graph replay after the lengths changed on the device")
+    out.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    fresh_o, fresh_l, _ = binding.decode(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(out, fresh_o) and torch.equal(lse, fresh_l), "replay on new lengths differs"
+    ref_o, ref_l = oracle_rows(inp.to("cpu"), rows=rows)
+    compare(fresh_o, fresh_l, ref_o, ref_l, "bf16", rows=rows, what="graph replay on new lengths")
+
+
 # ------------------------------------------------------------------ full-size workloads (sampled rows)
 
 FULL = ["r1_b128_h16_kv1k-8k_bf16", "mtp3_b64_h32_kv80k_fp8", "mtp7_b32_h128_kv16k-32k_bf16",
