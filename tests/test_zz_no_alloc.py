@@ -53,3 +53,45 @@ def test_noalloc_matches_the_workspace_entry_point_twice_then_refuses_oversize()
     assert ei.value.status == binding.MLA_ERR_SCRATCH_LIMIT
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
+
+
+def test_noalloc_replayed_from_a_graph():
+    """Captured in a HIP graph (its partials in the static buffer, no memset
+    recorded): three replays, each after the outputs were overwritten with
+    NaN and with a differently shaped eager call of the same entry point in
+    between (which reuses the buffer), equal the eager call bit for bit."""
+    inp = wl.make_inputs(3, 32, 4, [25000, 800, 18000], kv_dtype="fp8", out_dtype="bf16", seed=96).to(DEV)
+    other = wl.make_inputs(2, 16, 2, [3000, 40], kv_dtype="fp8", out_dtype="bf16", seed=97).to(DEV)
+    splits = 4
+
+    def call(x, out, lse, stream=None):
+        binding.mla_decode_fp8_noalloc(x.q_nope, x.q_pe, x.kv_cache, x.block_table, x.seq_lens, x.max_seq_len,
+                                       x.softmax_scale, x.q_scale, x.kv_scale, out, lse, splits, stream=stream)
+
+    shape = (inp.B, inp.T, inp.H, 512)
+    eager_o = torch.empty(shape, device=DEV, dtype=torch.bfloat16)
+    eager_l = torch.empty(shape[:3], device=DEV, dtype=torch.float32)
+    _say("[gpu] noalloc graph: eager call")
+    call(inp, eager_o, eager_l)
+    torch.cuda.synchronize()
+    out, lse = torch.empty_like(eager_o), torch.empty_like(eager_l)
+    o2 = torch.empty((other.B, other.T, other.H, 512), device=DEV, dtype=torch.bfloat16)
+    l2 = torch.empty((other.B, other.T, other.H), device=DEV, dtype=torch.float32)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call(inp, out, lse, stream=s)       # warm the stream
+        torch.cuda.synchronize()
+        _say("[gpu] noalloc graph: capture")
+        with torch.cuda.graph(g, stream=s):
+            call(inp, out, lse, stream=s)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        _say("[gpu] noalloc graph: replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), "replay %d differs" % rep
+        call(other, o2, l2)                 # reuses the static buffer between replays
+        torch.cuda.synchronize()
