@@ -759,6 +759,54 @@ def test_stage_one_then_merge_equals_one_call(kv_dtype):
     assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
 
 
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_partials_of_page_slices_merge_to_the_whole_sequence(kv_dtype):
+    """Stage two fed with partials from separate calls, as a sequence sharded
+    over W holders would produce them: each sequence's pages are cut into
+    W = 3 contiguous slices and stage one runs per slice.  Draft tokens are
+    flattened into the batch (q_len 1 per entry), so that each entry's length
+    is the prefix of the slice its query sees: the whole slice before the
+    causal limit, part of it at the limit, none after.  The slices' outputs
+    and LSEs, packed as [rows, W, 513] partials, are merged by
+    mla_merge_partials and compared with the oracle on the whole sequences
+    (empty slices and queries that see none of a slice included)."""
+    B, T, H, W = 3, 3, 16, 3
+    lens = [1000, 130, 2600]
+    full = wl.make_inputs(B, H, T, lens, kv_dtype=kv_dtype, out_dtype="f32", seed=22, poison=True)
+    n_pages = [(L + 63) // 64 for L in lens]
+    cuts = [[round(w * n / W) for w in range(W + 1)] for n in n_pages]
+    width = max(c[w + 1] - c[w] for c in cuts for w in range(W))
+    dev_kv = full.kv_cache.to(DEV)
+    rows = B * T * H
+    ws = torch.empty((rows, W, 513), device=DEV, dtype=torch.float32)
+    for w in range(W):
+        bt = torch.full((B * T, max(1, width)), -1, dtype=torch.int32)
+        sl = torch.zeros(B * T, dtype=torch.int32)
+        for b in range(B):
+            p0, p1 = cuts[b][w], cuts[b][w + 1]
+            slice_tokens = max(0, min(lens[b], p1 * 64) - p0 * 64)
+            for t in range(T):
+                bt[b * T + t, :p1 - p0] = full.block_table[b, p0:p1]
+                n_vis = lens[b] - T + t + 1                       # tokens query t sees in the whole sequence
+                sl[b * T + t] = min(max(n_vis - p0 * 64, 0), slice_tokens)
+        g = wl.DecodeInputs(full.q_nope.reshape(B * T, 1, H, -1).to(DEV), full.q_pe.reshape(B * T, 1, H, -1).to(DEV),
+                            dev_kv, bt.to(DEV), sl.to(DEV), None, kv_dtype, "f32", full.softmax_scale,
+                            full.q_scale, full.kv_scale, max_len=width * 64)
+        _say("[gpu] slice %d of %d (%s): lengths %s" % (w, W, kv_dtype, sl.tolist()))
+        o, l, _ = binding.decode(g, num_kv_splits=1)
+        torch.cuda.synchronize()
+        ws[:, w, :512] = o.reshape(rows, 512)
+        ws[:, w, 512] = l.reshape(rows)
+    out = torch.empty((B, T, H, 512), device=DEV, dtype=torch.float32)
+    lse = torch.empty((B, T, H), device=DEV, dtype=torch.float32)
+    binding.mla_merge_partials(ws, rows, W, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_rows(full)
+    e = compare(out, lse, ref_o, ref_l, kv_dtype, what="merged page slices %s" % kv_dtype)
+    _say("[gpu] merged page slices %s: max |out - oracle| %.4g, lse rel %.3g" % ((kv_dtype,) + e))
+
+
 # ------------------------------------------------------------------ the largest shapes the calls accept
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8", "sparse", "sparse_fp8"])
