@@ -87,9 +87,12 @@
  *    that violates this returns MLA_ERR_UNSUPPORTED (the library's own choice
  *    never does).  A failed launch returns MLA_ERR_HIP.
  *  - Device data is not validated on the host.  In the kernels, seq_lens are
- *    clamped to [0, max_blocks_per_seq * 64], page numbers outside
- *    [0, num_blocks) read as zero vectors, and block-table slots past a
- *    sequence's last page are never read.  seq_lens[b] must not exceed
+ *    clamped to [0, max_blocks_per_seq * 64], and block-table slots past a
+ *    sequence's last page are never read.  A page number outside
+ *    [0, num_blocks) is never dereferenced: in dense calls (and the MHA
+ *    route) its tokens read as zero vectors, which still take part in the
+ *    softmax with score 0; in sparse calls an index whose page is outside
+ *    that range is skipped, as an index outside [0, seq_lens[b]) is.  seq_lens[b] must not exceed
  *    max_seq_len (the host bound that sizes the splits); tokens beyond
  *    num_kv_splits chunks of the bound (beyond the bound itself, when the
  *    device cuts the pieces) are not attended.

@@ -481,6 +481,46 @@ def test_sparse_out_of_range_and_duplicate_indices(kv_dtype):
     check_full(inp, 0, "sparse odd indices")
 
 
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "sparse_bf16", "sparse_fp8"])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_invalid_page_ids_follow_the_stated_rule(kind, splits):
+    """Block-table entries inside a sequence that name no page of the pool
+    (past it, negative, far past it), checked against the rule the C header
+    states for each kind.  Dense: their tokens read as zero vectors, so the
+    call equals the oracle run with those entries pointing at an appended
+    all-zero page.  Sparse: an index whose page is invalid is skipped, so the
+    call equals the oracle run with those indices replaced by -1."""
+    kv_dtype = "fp8" if kind.endswith("fp8") else "bf16"
+    K = 200 if kind.startswith("sparse") else None
+    inp = wl.make_inputs(2, 16, 2, [300, 700], kv_dtype=kv_dtype, out_dtype="f32", topk=K, seed=23)
+    NB = inp.NB
+    bad = inp.block_table.clone()
+    bad[0, 2] = NB + 5
+    bad[1, 1] = -3
+    bad[1, 7] = 1 << 30
+    inp.block_table = bad
+    out, lse = run_case(inp, splits, "invalid page ids %s" % kind)
+    invalid = (bad < 0) | (bad >= NB)
+    if K is None:
+        zero_page = torch.zeros_like(inp.kv_cache[:1])
+        ref_in = wl.DecodeInputs(inp.q_nope, inp.q_pe, torch.cat([inp.kv_cache, zero_page]),
+                                 torch.where(invalid, torch.full_like(bad, NB), bad), inp.seq_lens, None,
+                                 kv_dtype, "f32", inp.softmax_scale, inp.q_scale, inp.kv_scale)
+    else:
+        idx = inp.topk_indices.clone()
+        for b in range(inp.B):
+            slot = idx[b].clamp(min=0) // 64
+            in_seq = (idx[b] >= 0) & (idx[b] < int(inp.seq_lens[b]))
+            hit = in_seq & invalid[b][slot.clamp(max=inp.MB - 1).long()]
+            idx[b][hit] = -1
+        assert (idx != inp.topk_indices).any()
+        ref_in = wl.DecodeInputs(inp.q_nope, inp.q_pe, inp.kv_cache, bad.clamp(min=0, max=NB - 1), inp.seq_lens,
+                                 idx, kv_dtype, "f32", inp.softmax_scale, inp.q_scale, inp.kv_scale)
+    ref_o, ref_l = oracle_rows(ref_in)
+    compare(out, lse, ref_o, ref_l, kv_dtype, what="invalid page ids %s" % kind)
+
+
 def test_sparse_index_probe_histogram_exact():
     """q = 0 and latent c_j = e_(j mod 512): n * out is the exact histogram."""
     L, K = 2000, 1024
