@@ -521,6 +521,34 @@ def test_invalid_page_ids_follow_the_stated_rule(kind, splits):
     compare(out, lse, ref_o, ref_l, kv_dtype, what="invalid page ids %s" % kind)
 
 
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "sparse_bf16", "sparse_fp8"])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_seq_lens_outside_the_table_are_clamped(kind, splits):
+    """seq_lens -4 and 1000 with a five-page block table (and max_seq_len
+    1000): the kernels clamp them to [0, 320], as the C header states, so the
+    call equals the oracle on lengths 0 and 320 (sparse: indices between 320
+    and 1000 are then outside the sequence and skipped)."""
+    kv_dtype = "fp8" if kind.endswith("fp8") else "bf16"
+    K = 128 if kind.startswith("sparse") else None
+    inp = wl.make_inputs(2, 16, 2, [300, 320], kv_dtype=kv_dtype, out_dtype="f32", topk=K, seed=24)
+    assert inp.MB == 5
+    idx = None
+    if K is not None:
+        idx = inp.topk_indices.clone()
+        idx[1, :, :16] = torch.arange(320, 1000, 45, dtype=idx.dtype)[:16]
+    ref_in = wl.DecodeInputs(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table,
+                             torch.tensor([0, 320], dtype=torch.int32), idx, kv_dtype, "f32", inp.softmax_scale,
+                             inp.q_scale, inp.kv_scale)
+    call_in = wl.DecodeInputs(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table,
+                              torch.tensor([-4, 1000], dtype=torch.int32), idx, kv_dtype, "f32", inp.softmax_scale,
+                              inp.q_scale, inp.kv_scale, max_len=1000)
+    out, lse = run_case(call_in, splits, "seq_lens clamped %s" % kind)
+    ref_o, ref_l = oracle_rows(ref_in)
+    compare(out, lse, ref_o, ref_l, kv_dtype, what="seq_lens clamped %s" % kind)
+    assert torch.isneginf(lse[0]).all().item() and torch.count_nonzero(out[0]).item() == 0
+
+
 def test_sparse_index_probe_histogram_exact():
     """q = 0 and latent c_j = e_(j mod 512): n * out is the exact histogram."""
     L, K = 2000, 1024
