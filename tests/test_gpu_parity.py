@@ -88,6 +88,39 @@ def test_dense_bf16_shapes(H, T, lens, splits):
     check_full(inp, splits, "dense bf16 H=%d T=%d" % (H, T))
 
 
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "sparse_bf16", "sparse_fp8"])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_no_lse_in_every_kind(kind, splits):
+    """lse = NULL (out only) through each entry point, written by the partial
+    kernel (one split) or by the merge (three)."""
+    kv_dtype = "fp8" if kind.endswith("fp8") else "bf16"
+    K = 160 if kind.startswith("sparse") else None
+    inp = wl.make_inputs(3, 16, 2, [90, 400, 1], kv_dtype=kv_dtype, out_dtype="bf16", topk=K, seed=25)
+    g = inp.to(DEV)
+    out = torch.full((3, 2, 16, 512), float("nan"), device=DEV, dtype=torch.bfloat16)
+    _say("[gpu] no lse %s splits=%d" % (kind, splits))
+    fp8 = kv_dtype == "fp8"
+    need = binding.workspace_size(g.B, g.T, g.H, g.max_seq_len, g.K, fp8, splits)
+    ws = torch.empty((need + 3) // 4, device=DEV, dtype=torch.float32) if need > 0 else None
+    assert (need > 0) == (splits > 1)
+    if K is not None and fp8:
+        binding.mla_sparse_decode_fp8(g.q_nope, g.q_pe, g.kv_cache, g.block_table, g.seq_lens, g.topk_indices,
+                                      g.max_seq_len, g.softmax_scale, g.q_scale, g.kv_scale, out, None, ws, splits)
+    elif K is not None:
+        binding.mla_sparse_decode(g.q_nope, g.q_pe, g.kv_cache, g.block_table, g.seq_lens, g.topk_indices,
+                                  g.max_seq_len, g.softmax_scale, out, None, ws, splits)
+    elif fp8:
+        binding.mla_decode_fp8(g.q_nope, g.q_pe, g.kv_cache, g.block_table, g.seq_lens, g.max_seq_len,
+                               g.softmax_scale, g.q_scale, g.kv_scale, out, None, ws, splits)
+    else:
+        binding.mla_decode(g.q_nope, g.q_pe, g.kv_cache, g.block_table, g.seq_lens, g.max_seq_len, g.softmax_scale,
+                           out, None, ws, splits)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_rows(inp)
+    compare(out, torch.tensor(ref_l), ref_o, ref_l, kv_dtype, what="no lse %s" % kind)
+
+
 def test_dense_bf16_out_bf16_and_no_lse():
     inp = wl.make_inputs(2, 16, 2, [90, 400], kv_dtype="bf16", out_dtype="bf16", seed=3)
     g = inp.to(DEV)
