@@ -908,6 +908,30 @@ def test_partials_of_page_slices_merge_to_the_whole_sequence(kv_dtype):
     _say("[gpu] merged page slices %s: max |out - oracle| %.4g, lse rel %.3g" % ((kv_dtype,) + e))
 
 
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_sparse_stage_one_then_merge_equals_one_call(kv_dtype):
+    """The two-stage form through the sparse entry points (per-draft-token
+    lists): stage one alone (out = lse = NULL) into a workspace of NaN, then
+    mla_merge_partials, equal to the one-call form bit for bit."""
+    inp = wl.make_inputs(3, 40, 2, [100, 700, 1500], kv_dtype=kv_dtype, out_dtype="f32", topk=300,
+                         seed=26).to(DEV)
+    _say("[gpu] two-stage sparse %s" % kv_dtype)
+    ref_o, ref_l, ws = binding.decode(inp, num_kv_splits=3)
+    out, lse = torch.empty_like(ref_o), torch.empty_like(ref_l)
+    ws.fill_(float("nan"))
+    if kv_dtype == "fp8":
+        binding.mla_sparse_decode_fp8(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens,
+                                      inp.topk_indices, inp.max_seq_len, inp.softmax_scale, inp.q_scale,
+                                      inp.kv_scale, None, None, ws, 3)
+    else:
+        binding.mla_sparse_decode(inp.q_nope, inp.q_pe, inp.kv_cache, inp.block_table, inp.seq_lens,
+                                  inp.topk_indices, inp.max_seq_len, inp.softmax_scale, None, None, ws, 3)
+    binding.mla_merge_partials(ws, inp.B * inp.T * inp.H, 3, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+
+
 # ------------------------------------------------------------------ the largest shapes the calls accept
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8", "sparse", "sparse_fp8"])
