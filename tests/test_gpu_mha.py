@@ -246,3 +246,37 @@ def test_dense_mha_graph_replay():
     assert np.all(np.abs(o - ref_o) <= allowed)
     l = eager_l.double().cpu().reshape(-1).numpy()
     assert np.array_equal(np.isneginf(l), np.isneginf(ref_l))
+
+
+def test_dense_mha_invalid_pages_clamped_lengths_and_no_lse():
+    """The cache rules the C header gives the decode calls, through the MHA
+    route: block-table entries naming no page (past the pool, negative) read
+    as zero latents and zero rope parts, seq_lens -4 and 1000 with a
+    five-page table (max_seq_len 1000) clamp to 0 and 320, and lse = NULL.
+    Checked against the oracle on the equivalent valid input (the bad
+    entries pointing at an appended zero page, the clamped lengths)."""
+    inp = wl.make_inputs(3, 8, 4, [300, 320, 200], kv_dtype="bf16", out_dtype="f32", seed=215)
+    q, w_uk, w_uv = wl.mha_inputs(inp, seed=315)
+    assert inp.MB == 5
+    NB = inp.NB
+    bad = inp.block_table.clone()
+    bad[2, 1] = NB + 3
+    bad[2, 3] = -2
+    call_in = wl.DecodeInputs(inp.q_nope, inp.q_pe, inp.kv_cache, bad, torch.tensor([-4, 1000, 200], dtype=torch.int32),
+                              None, "bf16", "f32", inp.softmax_scale, max_len=1000)
+    g = call_in.to(DEV)
+    out = torch.full((inp.B, inp.T, inp.H, 128), float("nan"), device=DEV, dtype=torch.float32)
+    _say("[gpu] mha: invalid pages, clamped lengths, no lse")
+    binding.mla_dense_mha(q.to(DEV), g.q_pe, g.kv_cache, g.block_table, g.seq_lens, w_uk.to(DEV), w_uv.to(DEV),
+                          g.max_seq_len, g.softmax_scale, out, None)
+    torch.cuda.synchronize()
+    invalid = (bad < 0) | (bad >= NB)
+    ref_in = wl.DecodeInputs(inp.q_nope, inp.q_pe, torch.cat([inp.kv_cache, torch.zeros_like(inp.kv_cache[:1])]),
+                             torch.where(invalid, torch.full_like(bad, NB), bad),
+                             torch.tensor([0, 320, 200], dtype=torch.int32), None, "bf16", "f32", inp.softmax_scale)
+    ref_o, _ = oracle_mha(ref_in, q, w_uk, w_uv)
+    o = out.double().cpu().reshape(-1, 128).numpy()
+    err = float(np.abs(o - ref_o).max())
+    assert np.all(np.isfinite(o)) and err <= TOL, "max |out - oracle| = %.3g" % err
+    assert not np.any(o[: inp.T * inp.H]), "the empty sequence's rows must be 0"
+    _say("[gpu] mha invalid pages / clamped lengths: max |out - oracle| %.4g" % err)
