@@ -280,3 +280,14 @@ def test_dense_mha_invalid_pages_clamped_lengths_and_no_lse():
     assert np.all(np.isfinite(o)) and err <= TOL, "max |out - oracle| = %.3g" % err
     assert not np.any(o[: inp.T * inp.H]), "the empty sequence's rows must be 0"
     _say("[gpu] mha invalid pages / clamped lengths: max |out - oracle| %.4g" % err)
+
+
+def test_dense_mha_maximum_query_count():
+    """The largest q_len the route accepts (MLA_MHA_MAX_Q_LEN = 65536): one
+    65536-token prefill, one head; the first and last 64 queries and a random
+    sample against the oracle."""
+    T = binding.MHA_MAX_Q_LEN
+    inp = wl.make_inputs(1, 1, T, [T], kv_dtype="bf16", out_dtype="bf16", seed=216)
+    q, w_uk, w_uv = wl.mha_inputs(inp, seed=316)
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(T - 64, T), sample_rows(T, 96, seed=216)]))
+    check(inp, q, w_uk, w_uv, "q_len %d" % T, rows=rows, out_dtype="bf16")
