@@ -334,7 +334,8 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
 
   const float c_qk = p.qk_scale;   // softmax scale * log2(e)
   float m = -INFINITY;             // running maximum (log2 domain), per query
-  float l = 0.f;                   // this half's sum of the rounded weights
+  float l = 0.f;                   // this half's sum of the rounded weights (normalizes O)
+  float lx = 0.f;                  // this half's sum of the unrounded weights (the LSE)
   f32x16_t o[4] = {f32x16_t{}, f32x16_t{}, f32x16_t{}, f32x16_t{}};   // O^T, dims 32 f .. 32 f + 31
   const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
 
@@ -384,18 +385,21 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
       const float m_new = fmaxf(m, tmax == -INFINITY ? -INFINITY : tmax * c_qk);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
       const float nsh = m_new == -INFINITY ? 0.f : -m_new;
-      float ls = 0.f;
+      float ls = 0.f, lsx = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const bf16x2_t pr = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][i], c_qk, nsh)),
-                               (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c_qk, nsh))};
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_qk, nsh));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c_qk, nsh));
+          const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
           ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
+          lsx += e0 + e1;
           pb[kb][i / 8][i % 8] = pr[0];
           pb[kb][i / 8][i % 8 + 1] = pr[1];
         }
       l = l * alpha + ls;
+      lx = lx * alpha + lsx;
       m = m_new;
       if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -423,6 +427,7 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
   }
 
   const float l_tot = l + __shfl_xor(l, 32);
+  const float lx_tot = lx + __shfl_xor(lx, 32);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   if (!t_ok) return;
@@ -442,7 +447,7 @@ __global__ void __launch_bounds__(256, 2) mha_attn_kernel(const MhaParams p) {
         *(bf16x4_t*)op = v;
       }
     }
-  if (hh == 0 && p.lse) p.lse[orow] = empty ? -INFINITY : (m + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  if (hh == 0 && p.lse) p.lse[orow] = empty ? -INFINITY : (m + __builtin_amdgcn_logf(lx_tot)) * kLn2;
 }
 
 unsigned grid_of(int64_t work) { return (unsigned)((work + 7) / 8 * 8); }
