@@ -291,3 +291,35 @@ def test_dense_mha_maximum_query_count():
     q, w_uk, w_uv = wl.mha_inputs(inp, seed=316)
     rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(T - 64, T), sample_rows(T, 96, seed=216)]))
     check(inp, q, w_uk, w_uv, "q_len %d" % T, rows=rows, out_dtype="bf16")
+
+
+def test_dense_mha_lse_over_two_nearly_equal_keys():
+    """One query over two keys whose second weight lies just under 1 (swept
+    over 64 heads across several bf16 steps): lse = ln(1 + w2) exactly.  A
+    sum of the bf16-rounded weights would be off by up to about 0.001 here
+    (half a bf16 step of w2, over 1 + w2), at the 1e-3 bound; the LSE must
+    follow the unrounded weights."""
+    H = 64
+    inp = wl.make_inputs(1, H, 1, [2], kv_dtype="bf16", out_dtype="f32", seed=217)
+    q, w_uk, w_uv = wl.mha_inputs(inp, seed=317)
+    q = torch.zeros_like(q)                                  # no-rope part: no contribution
+    q_pe = torch.zeros_like(inp.q_pe)
+    q_pe[0, 0, :, 0] = (1.0 + torch.arange(H, dtype=torch.float32) / H).to(q_pe.dtype)
+    kv = inp.kv_cache.clone()
+    page = int(inp.block_table[0, 0])
+    kv[page, :2] = 0
+    kv[page, 1, 512] = torch.tensor(-0.0271, dtype=torch.float32).to(kv.dtype)   # rope dim 0 of key 1
+    inp = wl.DecodeInputs(inp.q_nope, q_pe, kv, inp.block_table, inp.seq_lens, None, "bf16", "f32",
+                          inp.softmax_scale)
+    out, lse = run_mha(inp, q, w_uk, w_uv)
+    x = float(kv[page, 1, 512].float())
+    a = q_pe[0, 0, :, 0].double()
+    w2 = torch.exp(inp.softmax_scale * a * x)
+    assert float(w2.min()) > 0.99 and float(w2.max()) < 1.0
+    ref = torch.log1p(w2)
+    err = float((lse[0, 0].double().cpu() - ref).abs().max())
+    _say("[gpu] mha two near-equal keys: w2 in [%.5f, %.5f], max |lse - ln(1 + w2)| %.3g"
+         % (float(w2.min()), float(w2.max()), err))
+    assert err < 1e-5, "LSE follows rounded weights: %.3g" % err
+    ref_o, _ = oracle_mha(inp, q, w_uk, w_uv)
+    assert np.abs(out.double().cpu().reshape(-1, 128).numpy() - ref_o).max() <= TOL
