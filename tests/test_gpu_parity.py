@@ -582,6 +582,47 @@ def test_seq_lens_outside_the_table_are_clamped(kind, splits):
     assert torch.isneginf(lse[0]).all().item() and torch.count_nonzero(out[0]).item() == 0
 
 
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "sparse_bf16", "sparse_fp8"])
+def test_lse_over_two_nearly_equal_keys(kind):
+    """One query over two keys whose second weight lies just under 1 (swept
+    over 64 heads across several rounding steps of the weights' format):
+    lse = ln(1 + w2) exactly.  The weights enter the value product rounded
+    to bf16 or e4m3; a sum of the rounded weights would be off by up to half
+    a step of w2 over 1 + w2 (about 1e-3 for bf16, 3e-2 for e4m3), so the
+    LSE must follow the unrounded weights."""
+    H = 64
+    fp8 = kind.endswith("fp8")
+    K = 2 if kind.startswith("sparse") else None
+    base = wl.make_inputs(1, H, 1, [2], kv_dtype="bf16", out_dtype="f32", topk=K, seed=27)
+    page = int(base.block_table[0, 0])
+    a = 1.0 + torch.arange(H, dtype=torch.float32) / H
+    x = -0.02734375                                   # exact in bf16 and e4m3
+    q_nope = torch.zeros((1, 1, H, 512), dtype=torch.float32)
+    q_pe = torch.zeros((1, 1, H, 64), dtype=torch.float32)
+    q_pe[0, 0, :, 0] = a
+    kv = torch.zeros_like(base.kv_cache, dtype=torch.float32)
+    kv[page, 1, 512] = x
+    if fp8:
+        enc = lambda t: t.to(torch.float8_e4m3fn).view(torch.uint8)   # noqa: E731
+        q_nope, q_pe, kv = enc(q_nope), enc(q_pe), enc(kv)
+        a = q_pe[0, 0, :, 0].view(torch.float8_e4m3fn).float()        # the query as stored
+    else:
+        q_nope, q_pe, kv = q_nope.to(torch.bfloat16), q_pe.to(torch.bfloat16), kv.to(torch.bfloat16)
+        a = q_pe[0, 0, :, 0].float()
+    idx = None if K is None else torch.tensor([[[0, 1]]], dtype=torch.int32)
+    inp = wl.DecodeInputs(q_nope, q_pe, kv, base.block_table, base.seq_lens, idx, "fp8" if fp8 else "bf16", "f32",
+                          base.softmax_scale, 1.0, 1.0)
+    out, lse = run_case(inp, 0, "two near-equal keys %s" % kind)
+    w2 = torch.exp(base.softmax_scale * a.double() * x)
+    assert float(w2.min()) > 0.99 and float(w2.max()) < 1.0
+    err = float((lse[0, 0].double().cpu() - torch.log1p(w2)).abs().max())
+    _say("[gpu] two near-equal keys %s: w2 in [%.5f, %.5f], max |lse - ln(1 + w2)| %.3g"
+         % (kind, float(w2.min()), float(w2.max()), err))
+    assert err < 1e-5, "LSE follows rounded weights: %.3g" % err
+    assert torch.count_nonzero(out).item() == 0
+
+
 def test_sparse_index_probe_histogram_exact():
     """q = 0 and latent c_j = e_(j mod 512): n * out is the exact histogram."""
     L, K = 2000, 1024
