@@ -334,3 +334,32 @@ def test_product_path_fails_loudly_without_the_library_or_a_gpu(monkeypatch):
     inp = wl.make_inputs(1, 16, 1, [40], kv_dtype="bf16", out_dtype="f32", seed=3)
     with pytest.raises(ValueError, match="GPU"):
         binding.decode(inp)
+
+
+def test_benchmark_reference_library_rejects_bad_arguments():
+    """The benchmark's reference library (streaming read, LDS read rate)
+    loads and refuses bad arguments before touching a device."""
+    path = os.path.join(ROOT, "mla_paged_latent_03_amd", "libmla_stream_ref.so")
+    if not os.path.exists(path):
+        from mla_paged_latent_03_amd import build
+        build.build()
+    ref = ctypes.CDLL(path)
+    sr = ref.mla_stream_read_reference
+    sr.restype = ctypes.c_int
+    sr.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fake = ctypes.c_void_p(1 << 20)                 # never dereferenced: every case fails validation
+    assert sr(None, 36864, 1, fake, None) == 1       # no source
+    assert sr(fake, 36864, 0, fake, None) == 1       # no workgroups
+    assert sr(fake, 1000, 1, fake, None) == 1        # not a whole number of tiles
+    assert sr(ctypes.c_void_p((1 << 20) + 8), 36864, 1, fake, None) == 1   # misaligned source
+    lr = ref.mla_lds_read_rate_reference
+    lr.restype = ctypes.c_int
+    lr.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+    khz = ctypes.c_int(0)
+    assert lr(3, 8, 1, 1, fake, fake, ctypes.byref(khz), None) == 1      # waves not 1, 2, 4, 8 or 16
+    assert lr(4, 5, 1, 1, fake, fake, ctypes.byref(khz), None) == 1      # reads in flight not 2, 4, 8 or 16
+    assert lr(4, 8, 0, 1, fake, fake, ctypes.byref(khz), None) == 1      # no workgroups
+    assert lr(4, 8, 1, 0, fake, fake, ctypes.byref(khz), None) == 1      # no iterations
+    assert lr(4, 8, 1, 1, None, fake, ctypes.byref(khz), None) == 1      # no sink
+    assert lr(4, 8, 1, 1, fake, fake, None, None) == 1                   # no clock-rate output
