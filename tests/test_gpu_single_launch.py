@@ -171,3 +171,56 @@ def test_single_launch_random_shapes(case):
         torch.cuda.synchronize()
     ref_o, ref_l = oracle_rows(inp)
     compare(out, lse, ref_o, ref_l, kv_dtype, what=what)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "sparse_bf16", "sparse_fp8"])
+def test_device_data_rules_and_no_lse_match_two_launches(kind):
+    """Invalid page ids, a seq_len past the block table (within max_seq_len)
+    and lse = NULL through the single-launch form: the same bits as the two
+    launches, with and without lse."""
+    kv_dtype = "fp8" if kind.endswith("fp8") else "bf16"
+    K = 200 if kind.startswith("sparse") else None
+    inp = wl.make_inputs(2, 16, 2, [300, 700], kv_dtype=kv_dtype, out_dtype="f32", topk=K, seed=157)
+    bad = inp.block_table.clone()
+    bad[0, 2] = inp.NB + 5
+    bad[1, 1] = -3
+    inp.block_table = bad
+    inp.seq_lens = torch.tensor([300, 5000], dtype=torch.int32)     # 5000 clamps to the 11-page table
+    inp.max_len = 5000
+    splits = 3
+    assert _fused_planned(inp, splits)
+    g = inp.to(DEV)
+    fp8 = kv_dtype == "fp8"
+    _say("[gpu] single launch: device-data rules, %s" % kind)
+    results = []
+    for fused in (False, True):
+        old = os.environ.get("MLA_SINGLE_LAUNCH")
+        if fused:
+            os.environ["MLA_SINGLE_LAUNCH"] = "1"
+        try:
+            o, l, _ = binding.decode(g, num_kv_splits=splits)
+            need = binding.workspace_size(g.B, g.T, g.H, g.max_seq_len, g.K, fp8, splits)
+            ws = torch.empty((need + 3) // 4, device=DEV, dtype=torch.float32)
+            o_nl = torch.full_like(o, float("nan"))
+            if K is not None and fp8:
+                binding.mla_sparse_decode_fp8(g.q_nope, g.q_pe, g.kv_cache, g.block_table, g.seq_lens, g.topk_indices,
+                                              g.max_seq_len, g.softmax_scale, g.q_scale, g.kv_scale, o_nl, None, ws,
+                                              splits)
+            elif K is not None:
+                binding.mla_sparse_decode(g.q_nope, g.q_pe, g.kv_cache, g.block_table, g.seq_lens, g.topk_indices,
+                                          g.max_seq_len, g.softmax_scale, o_nl, None, ws, splits)
+            elif fp8:
+                binding.mla_decode_fp8(g.q_nope, g.q_pe, g.kv_cache, g.block_table, g.seq_lens, g.max_seq_len,
+                                       g.softmax_scale, g.q_scale, g.kv_scale, o_nl, None, ws, splits)
+            else:
+                binding.mla_decode(g.q_nope, g.q_pe, g.kv_cache, g.block_table, g.seq_lens, g.max_seq_len,
+                                   g.softmax_scale, o_nl, None, ws, splits)
+            torch.cuda.synchronize()
+        finally:
+            if old is None:
+                os.environ.pop("MLA_SINGLE_LAUNCH", None)
+            else:
+                os.environ["MLA_SINGLE_LAUNCH"] = old
+        assert torch.isfinite(o).all().item() and torch.equal(o, o_nl)
+        results.append((o, l))
+    assert torch.equal(results[0][0], results[1][0]) and torch.equal(results[0][1], results[1][1])
