@@ -623,6 +623,47 @@ def test_lse_over_two_nearly_equal_keys(kind):
     assert torch.count_nonzero(out).item() == 0
 
 
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_lse_over_two_nearly_equal_keys_after_a_jump(kv_dtype):
+    """Two 20000-token units, one split (the four-wave kernels; fp8: the
+    feature-split kernel, over 16384 tokens) whose keys all score -32 to -64
+    except two near-equal ones in the middle: for the heads with the larger
+    scores the row maximum jumps by more than the 64 (log2) the first tile's
+    reference allows, so the second pass runs, for the others it does not;
+    either way the LSE must equal ln(1 + w2) to 1e-5."""
+    B, T, H, L = 2, 1, 128, 20000
+    fp8 = kv_dtype == "fp8"
+    assert binding.launch_waves(B, T, H, L, 0, fp8) == 4
+    base = wl.make_inputs(B, H, T, [L, L], kv_dtype="bf16", out_dtype="f32", seed=28)
+    a = 1.0 + torch.arange(H, dtype=torch.float32) % 64 / 64
+    x = -0.02734375
+    q_nope = torch.zeros((B, T, H, 512), dtype=torch.float32)
+    q_pe = torch.zeros((B, T, H, 64), dtype=torch.float32)
+    q_pe[:, 0, :, 0] = a
+    kv = torch.zeros_like(base.kv_cache, dtype=torch.float32)
+    tok = torch.arange(L)
+    for b, j in ((0, 10000), (1, 17)):
+        pages = base.block_table[b].long()
+        kv[pages[tok // 64], tok % 64, 512] = -448.0                  # weights below 1e-14
+        kv[pages[j // 64], j % 64, 512] = 0.0
+        kv[pages[(j + 1) // 64], (j + 1) % 64, 512] = x
+    if fp8:
+        enc = lambda t: t.to(torch.float8_e4m3fn).view(torch.uint8)   # noqa: E731
+        q_nope, q_pe, kv = enc(q_nope), enc(q_pe), enc(kv)
+        a = q_pe[0, 0, :, 0].view(torch.float8_e4m3fn).float()
+    else:
+        q_nope, q_pe, kv = q_nope.to(torch.bfloat16), q_pe.to(torch.bfloat16), kv.to(torch.bfloat16)
+        a = q_pe[0, 0, :, 0].float()
+    inp = wl.DecodeInputs(q_nope, q_pe, kv, base.block_table, base.seq_lens, None, kv_dtype, "f32",
+                          base.softmax_scale, 1.0, 1.0)
+    out, lse = run_case(inp, 1, "two near-equal keys after a jump %s" % kv_dtype)
+    w2 = torch.exp(base.softmax_scale * a.double() * x)
+    err = float((lse[:, 0].double().cpu() - torch.log1p(w2)[None, :]).abs().max())
+    _say("[gpu] two near-equal keys after a jump %s: max |lse - ln(1 + w2)| %.3g" % (kv_dtype, err))
+    assert err < 1e-5, "LSE off: %.3g" % err
+    assert torch.count_nonzero(out).item() == 0
+
 def test_sparse_index_probe_histogram_exact():
     """q = 0 and latent c_j = e_(j mod 512): n * out is the exact histogram."""
     L, K = 2000, 1024
