@@ -95,3 +95,25 @@ def test_noalloc_replayed_from_a_graph():
         assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), "replay %d differs" % rep
         call(other, o2, l2)                 # reuses the static buffer between replays
         torch.cuda.synchronize()
+
+
+def test_noalloc_at_the_largest_workspace_it_holds():
+    """B = 127 sequences of 128 rows with two splits need 99.4% of the static
+    buffer (one more sequence would not fit and is refused): the call equals
+    the workspace entry point bit for bit, and a smaller call after it too."""
+    splits = 2
+    inp = wl.make_inputs(127, 32, 4, (150, 260), kv_dtype="fp8", out_dtype="bf16", seed=98).to(DEV)
+    need = binding.workspace_size(inp.B, inp.T, inp.H, inp.max_seq_len, 0, True, splits)
+    assert 0.99 * binding.STATIC_SCRATCH_BYTES < need <= binding.STATIC_SCRATCH_BYTES
+    assert binding.workspace_size(inp.B + 1, inp.T, inp.H, inp.max_seq_len, 0, True, splits) > \
+        binding.STATIC_SCRATCH_BYTES
+    for x in (inp, wl.make_inputs(3, 32, 4, [220, 90, 1], kv_dtype="fp8", out_dtype="bf16", seed=99).to(DEV)):
+        _say("[gpu] noalloc near the buffer limit: B=%d, workspace %d bytes" %
+             (x.B, binding.workspace_size(x.B, x.T, x.H, x.max_seq_len, 0, True, splits)))
+        ref_o, ref_l, _ = binding.decode(x, num_kv_splits=splits)
+        out = torch.full_like(ref_o, float("nan"))
+        lse = torch.full_like(ref_l, float("nan"))
+        binding.mla_decode_fp8_noalloc(x.q_nope, x.q_pe, x.kv_cache, x.block_table, x.seq_lens, x.max_seq_len,
+                                       x.softmax_scale, x.q_scale, x.kv_scale, out, lse, splits)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
