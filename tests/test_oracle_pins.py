@@ -384,6 +384,33 @@ def test_bf16_expanded_mha_rounds_the_expanded_keys_and_values():
     assert np.array_equal(o_e, o_f) and np.array_equal(l_e, l_f)
 
 
+
+def test_mha_oracle_two_keys_closed_form():
+    """Zero latents (so zero no-rope keys and zero values) and rope keys 0 and
+    x along one dimension: for a query whose rope part is a along it, the
+    weights are 1 and exp(scale a x), so lse = ln(1 + exp(scale a x)) and the
+    output is 0; a query that sees only the first key gets lse = 0.  Holds in
+    both expansion modes."""
+    import oracle.mha_bruteforce as mb
+    H, T, P = 4, 2, 16
+    a = np.array([1.0, 1.25, 1.5, 1.75])
+    x = -0.02734375
+    kv = np.zeros((1, P, 576))
+    kv[0, 1, 512] = x
+    bt = np.array([[0]], dtype=np.int32)
+    q_nope = np.random.default_rng(44).standard_normal((1, T, H, 128))
+    q_pe = np.zeros((1, T, H, 64))
+    q_pe[0, :, :, 0] = a
+    w = np.random.default_rng(45).standard_normal((H, 128, 512))
+    scale = 1 / np.sqrt(192)
+    for mode in ("f64", "bf16"):
+        o, l = mb.mha_paged(q_nope, q_pe, kv, bt, np.array([2]), w, w, scale, expanded=mode)
+        l = l.reshape(1, T, H)
+        assert np.abs(o).max() == 0.0
+        assert np.allclose(l[0, 0], 0.0, atol=1e-15)                       # draft token 0 sees key 0 only
+        assert np.allclose(l[0, 1], np.log1p(np.exp(scale * a * x)), rtol=0, atol=1e-14)
+
+
 def test_parity_bound_half_ulp_of_bf16():
     """The parity bound for bf16 outputs adds half a bf16 ulp of the value:
     exact at powers of two, and never exceeded by torch's round-to-nearest
