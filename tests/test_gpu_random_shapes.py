@@ -20,7 +20,7 @@ from parity import compare, oracle_rows
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-N_CASES = 40
+N_CASES = 100
 PAIR_CAP = 1_200_000          # (row, attended token) pairs per case
 SPECIAL_LENS = [0, 1, 63, 64, 65, 127, 128, 129]
 
