@@ -168,7 +168,7 @@ def test_dense_mha_bench_size_sampled_rows():
 # page-edge ones among them), q_len from a decode step to a whole prefill, and
 # the output dtype, drawn together.  Rows beyond a few hundred are sampled
 # (first and last rows included), since the oracle expands each row's keys.
-def _draw_mha_cases(n=12, seed=20261204):
+def _draw_mha_cases(n=40, seed=20261204):
     g = np.random.default_rng(seed)
     cases = []
     for i in range(n):
